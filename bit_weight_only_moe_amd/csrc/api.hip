@@ -1,0 +1,340 @@
+// C ABI of the W4A16 MoE layer: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Every check runs before the first launch,
+// so a failing call enqueues nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 8;
+constexpr int kDecodeMaxT = 64;
+// Tokens are staged in LDS 8 at a time (8 * K * 2.125 bytes <= 64 KB).
+constexpr int kMaxDim = 3840;
+
+// Validate one packed matrix stack against expected shape (0 = any).
+int check_matrix(const moe_w4_matrix& m, const char* name, int E, int rows, int cols) {
+  if (m.fmt != MOE_FMT_NVFP4 && m.fmt != MOE_FMT_INT4_G64)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, m.fmt);
+  if (m.num_experts < 1 || m.rows < 1 || m.cols < 64)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad shape E=%d rows=%d cols=%d", name, m.num_experts, m.rows, m.cols);
+  if (m.cols % 64) return fail(MOE_ERR_INVALID_ARG, "%s: cols=%d is not a multiple of 64", name, m.cols);
+  if (m.cols > kMaxDim || m.rows > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: cols=%d > %d or rows=%d > 65536", name, m.cols, kMaxDim, m.rows);
+  if ((E && m.num_experts != E) || (rows && m.rows != rows) || (cols && m.cols != cols))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shape [%d, %d, %d] does not match expected [%d, %d, %d]", name,
+                m.num_experts, m.rows, m.cols, E, rows, cols);
+  if (!m.codes || !m.scales) return fail(MOE_ERR_INVALID_ARG, "%s: null codes or scales", name);
+  if (!aligned16(m.codes) || !aligned16(m.scales))
+    return fail(MOE_ERR_INVALID_ARG, "%s: codes/scales not 16-byte aligned", name);
+  if (m.fmt == MOE_FMT_NVFP4) {
+    if (!m.tensor_scale) return fail(MOE_ERR_INVALID_ARG, "%s: NVFP4 needs tensor_scale", name);
+  } else {
+    if (!m.zeros) return fail(MOE_ERR_INVALID_ARG, "%s: INT4 needs zeros", name);
+  }
+  return MOE_OK;
+}
+
+int check_ffn(const moe_ffn_weights& w, const char* name, int E, int H, int I) {
+  std::string n(name);
+  int rc;
+  if ((rc = check_matrix(w.gate, (n + ".gate").c_str(), E, I, H))) return rc;
+  if ((rc = check_matrix(w.up, (n + ".up").c_str(), E, I, H))) return rc;
+  if ((rc = check_matrix(w.down, (n + ".down").c_str(), E, H, I))) return rc;
+  if (w.up.fmt != w.gate.fmt || w.down.fmt != w.gate.fmt)
+    return fail(MOE_ERR_INVALID_ARG, "%s: gate/up/down formats differ", name);
+  return MOE_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* p) : base((char*)p) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + used) : nullptr;
+    used += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+size_t grouped_ws(int E, int I, int total_rows, Carve* c, int32_t** active, uint16_t** h) {
+  Carve tmp(nullptr);
+  Carve& cv = c ? *c : tmp;
+  int32_t* a = cv.take<int32_t>((size_t)E + 1);
+  uint16_t* hh = cv.take<uint16_t>((size_t)total_rows * I);
+  if (active) *active = a;
+  if (h) *h = hh;
+  return cv.used;
+}
+
+struct DecodeWs {
+  float* logits;
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_pos;
+  int32_t* active;
+  uint16_t* h_routed;
+  uint16_t* h_shared;
+  float* o_routed;
+  float* o_shared;
+  void* perm_ws;
+};
+
+size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
+  Carve c(base);
+  const int Is = L->shared ? L->shared->gate.rows : 0;
+  const size_t n = (size_t)T * L->k;
+  DecodeWs t;
+  t.logits = c.take<float>((size_t)T * L->E);
+  t.ids = c.take<int32_t>(n);
+  t.w = c.take<float>(n);
+  t.counts = c.take<int32_t>((size_t)L->E);
+  t.offsets = c.take<int32_t>((size_t)L->E + 1);
+  t.sorted_pairs = c.take<int32_t>(n);
+  t.pair_pos = c.take<int32_t>(n);
+  t.active = c.take<int32_t>((size_t)L->E + 1);
+  t.h_routed = c.take<uint16_t>(n * L->I);
+  t.h_shared = c.take<uint16_t>((size_t)T * Is);
+  t.o_routed = c.take<float>(n * L->H);
+  t.o_shared = c.take<float>((size_t)T * L->H);
+  t.perm_ws = c.take<char>(T > kDecodeMaxT ? moe::permute_ws_bytes(T, L->k, L->E) : 0);
+  if (d) *d = t;
+  return c.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream) {
+  if (!m || !out) return fail(MOE_ERR_INVALID_ARG, "moe_dequant_w4: null argument");
+  int rc = check_matrix(*m, "moe_dequant_w4.m", 0, 0, 0);
+  if (rc) return rc;
+  if (expert < 0 || expert >= m->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dequant_w4: expert %d out of [0, %d)", expert, m->num_experts);
+  if (!aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "moe_dequant_w4: out not 16-byte aligned");
+  const size_t e = (size_t)expert, R = (size_t)m->rows, C = (size_t)m->cols;
+  const uint8_t* codes = m->codes + e * R * (C / 2);
+  const uint8_t* scales = (const uint8_t*)m->scales + e * R * (m->fmt == MOE_FMT_NVFP4 ? C / 16 : (C / 64) * 2);
+  const uint8_t* zeros = m->zeros ? m->zeros + e * R * (C / 64) : nullptr;
+  const float* ts = m->tensor_scale ? m->tensor_scale + e : nullptr;
+  return hip_status(moe::launch_dequant_expert(m->fmt, m->rows, m->cols, codes, scales, zeros, ts, out,
+                                               as_stream(stream)),
+                    "moe_dequant_w4");
+}
+
+static int check_route_dims(const char* who, int T, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", who, T);
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d < 1", who, E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d > %d", who, E, kMaxExperts);
+  if (k < 1 || k > std::min(E, kMaxTopK))
+    return fail(MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E, %d)]", who, k, kMaxTopK);
+  return MOE_OK;
+}
+
+int moe_route(const uint16_t* x, const float* w_router, int T, int H, int E, int k, float* logits_out,
+              int32_t* topk_ids, float* topk_w, void* stream) {
+  int rc = check_route_dims("moe_route", T, E, k);
+  if (rc) return rc;
+  if (H < 64 || H % 64) return fail(MOE_ERR_INVALID_ARG, "moe_route: H=%d is not a positive multiple of 64", H);
+  if (!x || !w_router || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "moe_route: null argument");
+  if (!logits_out) return fail(MOE_ERR_INVALID_ARG, "moe_route: logits_out is required as scratch (fp32 [T, E])");
+  if (!aligned16(x) || !aligned16(w_router))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: x / w_router not 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe::launch_router_logits(x, w_router, T, H, E, logits_out, s);
+  if (e == hipSuccess) e = moe::launch_topk_softmax(logits_out, T, E, k, topk_ids, topk_w, s);
+  return hip_status(e, "moe_route");
+}
+
+int moe_topk_softmax(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, void* stream) {
+  int rc = check_route_dims("moe_topk_softmax", T, E, k);
+  if (rc) return rc;
+  if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "moe_topk_softmax: null argument");
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_topk_softmax(logits, T, E, k, topk_ids, topk_w, as_stream(stream)),
+                    "moe_topk_softmax");
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return moe::permute_ws_bytes(T, k, E);
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pairs, int32_t* pair_pos, const uint16_t* x, uint16_t* x_perm, int H, void* ws,
+                size_t ws_bytes, void* stream) {
+  int rc = check_route_dims("moe_permute", T, E, k);
+  if (rc) return rc;
+  if (!topk_ids || !counts || !offsets || !sorted_pairs || !pair_pos)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: null argument");
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both be NULL");
+  if (x && (H < 64 || H % 64 || !aligned16(x) || !aligned16(x_perm)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: H=%d / x alignment invalid for the gather", H);
+  if (ws_bytes < moe::permute_ws_bytes(T, k, E) || (!ws && moe::permute_ws_bytes(T, k, E)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: workspace %zu < %zu bytes", ws_bytes,
+                moe::permute_ws_bytes(T, k, E));
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_permute(topk_ids, T, k, E, counts, offsets, sorted_pairs, pair_pos, x, x_perm, H, ws,
+                                        as_stream(stream)),
+                    "moe_permute");
+}
+
+size_t moe_grouped_ffn_workspace_size(int E, int H, int I, int total_rows, int mode) {
+  (void)H;
+  (void)mode;
+  if (E < 1 || I < 1 || total_rows < 0) return 0;
+  return grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
+}
+
+int moe_grouped_w4a16_ffn(const moe_ffn_weights* w, int E, int H, int I, const uint16_t* x,
+                          const int32_t* sorted_pairs, int k, const int32_t* offsets, int total_rows, float* out,
+                          int mode, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !x || !offsets || !out) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: null argument");
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: E=%d < 1", E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: E=%d > %d", E, kMaxExperts);
+  if (H < 64 || H % 64 || I < 64 || I % 64)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: H=%d, I=%d must be positive multiples of 64", H, I);
+  if (total_rows < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: total_rows < 0");
+  if (sorted_pairs && k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: k=%d < 1", k);
+  if (mode != MOE_MODE_AUTO && mode != MOE_MODE_GEMV && mode != MOE_MODE_MFMA)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: unknown mode %d", mode);
+  int rc = check_ffn(*w, "moe_grouped_w4a16_ffn.w", E, H, I);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: x/out alignment");
+  const size_t need = grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: workspace %zu < %zu bytes", ws_bytes, need);
+  if (mode == MOE_MODE_MFMA)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: MFMA mode not available in this build");
+  if (total_rows == 0) return MOE_OK;
+  Carve c(ws);
+  int32_t* active;
+  uint16_t* h;
+  grouped_ws(E, I, total_rows, &c, &active, &h);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe::launch_active_list(offsets, E, active, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemv_ffn(w, active, offsets, sorted_pairs, k, std::min(E, total_rows), nullptr, 0, x, H, h,
+                             nullptr, out, nullptr, s);
+  return hip_status(e, "moe_grouped_w4a16_ffn");
+}
+
+int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* topk_w, const float* out_shared,
+                const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, void* stream) {
+  if (T < 0 || k < 1 || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "moe_combine: T=%d k=%d", T, k);
+  if (H < 64 || H % 64) return fail(MOE_ERR_INVALID_ARG, "moe_combine: H=%d not a positive multiple of 64", H);
+  if (!out_perm || !pair_pos || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: null argument");
+  if (!aligned16(out_perm) || (out_shared && !aligned16(out_shared)) || (y_f32 && !aligned16(y_f32)) ||
+      !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: tensors must be 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_combine(out_perm, pair_pos, topk_w, out_shared, residual, T, k, H, y, y_f32,
+                                        as_stream(stream)),
+                    "moe_combine");
+}
+
+static int check_layer(const moe_layer_weights* L, const char* who) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "%s: null layer", who);
+  int rc = check_route_dims(who, 0, L->E, L->k);
+  if (rc) return rc;
+  if (L->H < 64 || L->H % 64 || L->I < 64 || L->I % 64)
+    return fail(MOE_ERR_INVALID_ARG, "%s: H=%d, I=%d must be positive multiples of 64", who, L->H, L->I);
+  if (!L->w_router || !aligned16(L->w_router)) return fail(MOE_ERR_INVALID_ARG, "%s: w_router null/unaligned", who);
+  if ((rc = check_ffn(L->experts, "layer.experts", L->E, L->H, L->I))) return rc;
+  if (L->shared) {
+    const int Is = L->shared->gate.rows;
+    if ((rc = check_ffn(*L->shared, "layer.shared", 1, L->H, Is))) return rc;
+    if (L->shared->gate.fmt != L->experts.gate.fmt)
+      return fail(MOE_ERR_INVALID_ARG, "%s: shared expert format differs from the routed experts", who);
+  }
+  return MOE_OK;
+}
+
+size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T) {
+  if (!L || T < 0 || check_layer(L, "moe_layer_decode_workspace_size")) return 0;
+  return decode_ws(L, T, nullptr, nullptr);
+}
+
+int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T, uint16_t* y,
+                     int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L, "moe_layer_decode");
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: T=%d < 0", T);
+  if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: null x or y");
+  if ((ids_out == nullptr) != (w_out == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: ids_out and w_out must both be given or both be NULL");
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: x / y / residual must be 16-byte aligned");
+  const size_t need = decode_ws(L, T, nullptr, nullptr);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: workspace %zu < %zu bytes or not 256-byte aligned", ws_bytes,
+                need);
+  if (T == 0) return MOE_OK;
+  DecodeWs d;
+  decode_ws(L, T, ws, &d);
+  hipStream_t s = as_stream(stream);
+  const int E = L->E, k = L->k, H = L->H;
+  hipError_t e = moe::launch_router_logits(x, L->w_router, T, H, E, d.logits, s);
+  if (e != hipSuccess) return hip_status(e, "moe_layer_decode");
+  if (T <= kDecodeMaxT) {
+    e = moe::launch_decode_route(d.logits, T, E, k, d.ids, d.w, d.offsets, d.sorted_pairs, d.pair_pos, d.active,
+                                 ids_out, w_out, s);
+  } else {
+    e = moe::launch_topk_softmax(d.logits, T, E, k, d.ids, d.w, s);
+    if (e == hipSuccess)
+      e = moe::launch_permute(d.ids, T, k, E, d.counts, d.offsets, d.sorted_pairs, d.pair_pos,
+                              nullptr, nullptr, H, d.perm_ws, s);
+    if (e == hipSuccess) e = moe::launch_active_list(d.offsets, E, d.active, s);
+    if (e == hipSuccess && ids_out) {
+      e = hipMemcpyAsync(ids_out, d.ids, sizeof(int32_t) * T * k, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess) e = hipMemcpyAsync(w_out, d.w, sizeof(float) * T * k, hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (e == hipSuccess)
+    e = moe::launch_gemv_ffn(&L->experts, d.active, d.offsets, d.sorted_pairs, k, std::min(E, T * k), L->shared, T,
+                             x, H, d.h_routed, d.h_shared, d.o_routed, d.o_shared, s);
+  if (e == hipSuccess)
+    e = moe::launch_combine(d.o_routed, d.pair_pos, d.w, L->shared ? d.o_shared : nullptr, residual, T, k, H, y,
+                            nullptr, s);
+  return hip_status(e, "moe_layer_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// VALU GEMV building blocks for the decode path: packed 4-bit expert rows
+// streamed from HBM with 16-byte loads, dequantised in registers, and
+// dot-multiplied against a few token vectors staged in LDS (the
+// "expert-indexed GEMVs" of "[Model] Add Flint (RecursiveSI/flint)",
+// section "What happened").
+//
+// A row of K weights is cut into pieces of 32 weights (16 bytes of codes).
+// LPR lanes share a row; lane `lir` of the group takes pieces lir, lir+LPR,
+// ... so each load instruction of a lane group reads LPR*16 consecutive
+// bytes.  64/LPR rows are in flight per wave.
+//
+// Token staging in LDS, per token, K values:
+//   NVFP4: bf16 in natural order (the FP4 convert yields element pairs 2i, 2i+1);
+//   INT4:  bf16 permuted inside every 8-element chunk as x0 x4 x1 x5 x2 x6 x3 x7
+//          (the magic-number unpack yields nibble pairs (s, s+4)), plus the fp32
+//          sum of each 32-element piece, used to remove the +128 offset and
+//          the zero point: sum (q - z) x = sum (128 + q) x - (128 + z) sum x.
+#pragma once
+
+#include "common.cuh"
+
+namespace moe {
+
+// Stage one token row (K bf16 values from global) into LDS in the FMT layout.
+// Thread `tid` of `nthr` handles whole 32-element pieces.
+template <int FMT>
+MOE_DEV void stage_token(uint16_t* __restrict__ dst, float* __restrict__ dsum, const uint16_t* __restrict__ src,
+                         int K, int tid, int nthr) {
+  const int npieces = K / 32;
+  for (int p = tid; p < npieces; p += nthr) {
+    const uint4* s = (const uint4*)(src + 32 * p);
+    uint4* d = (uint4*)(dst + 32 * p);
+    if (FMT == kFmtNvfp4) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) d[c] = s[c];
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = s[c];
+        // elements 0..7 as 16-bit halves of v.x .. v.w
+        const uint32_t e0 = v.x & 0xffffu, e1 = v.x >> 16, e2 = v.y & 0xffffu, e3 = v.y >> 16;
+        const uint32_t e4 = v.z & 0xffffu, e5 = v.z >> 16, e6 = v.w & 0xffffu, e7 = v.w >> 16;
+        uint4 o;
+        o.x = e0 | (e4 << 16);
+        o.y = e1 | (e5 << 16);
+        o.z = e2 | (e6 << 16);
+        o.w = e3 | (e7 << 16);
+        d[c] = o;
+        sum += ((bf16_to_f32(e0) + bf16_to_f32(e1)) + (bf16_to_f32(e2) + bf16_to_f32(e3))) +
+               ((bf16_to_f32(e4) + bf16_to_f32(e5)) + (bf16_to_f32(e6) + bf16_to_f32(e7)));
+      }
+      dsum[p] = sum;
+    }
+  }
+}
+
+// Raw bytes of one 32-weight piece: 16 bytes of codes, its scale bits and zero.
+struct RawPiece {
+  uint4 c;
+  uint32_t s;
+  uint32_t z;
+};
+
+// Load piece p of a packed row.
+//   codes_row : K/2 bytes;  scales_row: NVFP4 K/16 e4m3 bytes, INT4 K/64 fp16
+//   zeros_row : INT4 K/64 bytes
+template <int FMT>
+MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t* __restrict__ scales_row,
+                            const uint8_t* __restrict__ zeros_row, int p) {
+  RawPiece r;
+  r.c = *(const uint4*)(codes_row + 16 * p);
+  if (FMT == kFmtNvfp4) {
+    r.s = *(const uint16_t*)(scales_row + 2 * p);
+    r.z = 0;
+  } else {
+    r.s = ((const uint16_t*)scales_row)[p >> 1];
+    r.z = zeros_row[p >> 1];
+  }
+  return r;
+}
+
+// Accumulate the dot products of piece p (already loaded) with nt <= NT
+// staged tokens into acc[t] (without the NVFP4 tensor scale).
+//   xs   : LDS tokens, token t at xs + t*xstride (bf16 elements)
+//   xsum : LDS piece sums (INT4), token t at xsum + t*sstride
+template <int FMT, int NT>
+MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs, int xstride,
+                       const float* __restrict__ xsum, int sstride, int nt, float (&acc)[NT]) {
+  moe_bf16x2 q[16];
+  float b0, b1, zc = 0.f;
+  const uint4 c = r.c;
+  if (FMT == kFmtNvfp4) {
+    b0 = e4m3_to_f32(r.s, 0);
+    b1 = e4m3_to_f32(r.s, 1);
+    q[0] = e2m1x2_to_bf16<0>(c.x); q[1] = e2m1x2_to_bf16<1>(c.x);
+    q[2] = e2m1x2_to_bf16<2>(c.x); q[3] = e2m1x2_to_bf16<3>(c.x);
+    q[4] = e2m1x2_to_bf16<0>(c.y); q[5] = e2m1x2_to_bf16<1>(c.y);
+    q[6] = e2m1x2_to_bf16<2>(c.y); q[7] = e2m1x2_to_bf16<3>(c.y);
+    q[8] = e2m1x2_to_bf16<0>(c.z); q[9] = e2m1x2_to_bf16<1>(c.z);
+    q[10] = e2m1x2_to_bf16<2>(c.z); q[11] = e2m1x2_to_bf16<3>(c.z);
+    q[12] = e2m1x2_to_bf16<0>(c.w); q[13] = e2m1x2_to_bf16<1>(c.w);
+    q[14] = e2m1x2_to_bf16<2>(c.w); q[15] = e2m1x2_to_bf16<3>(c.w);
+  } else {
+    b0 = f16_to_f32((unsigned short)r.s);
+    b1 = 0.f;
+    zc = 128.0f + (float)r.z;
+    q[0] = int4x2_to_bf16_off128<0>(c.x); q[1] = int4x2_to_bf16_off128<1>(c.x);
+    q[2] = int4x2_to_bf16_off128<2>(c.x); q[3] = int4x2_to_bf16_off128<3>(c.x);
+    q[4] = int4x2_to_bf16_off128<0>(c.y); q[5] = int4x2_to_bf16_off128<1>(c.y);
+    q[6] = int4x2_to_bf16_off128<2>(c.y); q[7] = int4x2_to_bf16_off128<3>(c.y);
+    q[8] = int4x2_to_bf16_off128<0>(c.z); q[9] = int4x2_to_bf16_off128<1>(c.z);
+    q[10] = int4x2_to_bf16_off128<2>(c.z); q[11] = int4x2_to_bf16_off128<3>(c.z);
+    q[12] = int4x2_to_bf16_off128<0>(c.w); q[13] = int4x2_to_bf16_off128<1>(c.w);
+    q[14] = int4x2_to_bf16_off128<2>(c.w); q[15] = int4x2_to_bf16_off128<3>(c.w);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < nt) {
+      const uint4* xp = (const uint4*)(xs + t * xstride + 32 * p);
+      const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+      float d0 = 0.f, d1 = 0.f;
+      d0 = dot2_bf16(q[0], x0.x, d0); d0 = dot2_bf16(q[1], x0.y, d0);
+      d0 = dot2_bf16(q[2], x0.z, d0); d0 = dot2_bf16(q[3], x0.w, d0);
+      d0 = dot2_bf16(q[4], x1.x, d0); d0 = dot2_bf16(q[5], x1.y, d0);
+      d0 = dot2_bf16(q[6], x1.z, d0); d0 = dot2_bf16(q[7], x1.w, d0);
+      d1 = dot2_bf16(q[8], x2.x, d1); d1 = dot2_bf16(q[9], x2.y, d1);
+      d1 = dot2_bf16(q[10], x2.z, d1); d1 = dot2_bf16(q[11], x2.w, d1);
+      d1 = dot2_bf16(q[12], x3.x, d1); d1 = dot2_bf16(q[13], x3.y, d1);
+      d1 = dot2_bf16(q[14], x3.z, d1); d1 = dot2_bf16(q[15], x3.w, d1);
+      if (FMT == kFmtNvfp4) {
+        acc[t] = fmaf(b0, d0, acc[t]);
+        acc[t] = fmaf(b1, d1, acc[t]);
+      } else {
+        acc[t] = fmaf(b0, fmaf(-zc, xsum[t * sstride + p], d0 + d1), acc[t]);
+      }
+    }
+  }
+}
+
+// A packed matrix stack as the kernels see it.
+struct MatDev {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint8_t* zeros;
+  const float* ts;
+  int rows, cols;
+};
+
+MOE_DEV const uint8_t* row_codes(const MatDev& m, int e, int r) {
+  return m.codes + ((size_t)e * m.rows + r) * (size_t)(m.cols / 2);
+}
+template <int FMT>
+MOE_DEV const uint8_t* row_scales(const MatDev& m, int e, int r) {
+  return m.scales + ((size_t)e * m.rows + r) * (size_t)(FMT == kFmtNvfp4 ? m.cols / 16 : (m.cols / 64) * 2);
+}
+MOE_DEV const uint8_t* row_zeros(const MatDev& m, int e, int r) {
+  return m.zeros ? m.zeros + ((size_t)e * m.rows + r) * (size_t)(m.cols / 64) : nullptr;
+}
+template <int FMT>
+MOE_DEV float tensor_scale(const MatDev& m, int e) {
+  return FMT == kFmtNvfp4 ? m.ts[e] : 1.0f;
+}
+
+// Lanes per row: the largest power of two <= 64 dividing K/32.
+inline int lanes_per_row(int K) {
+  int pieces = K / 32, l = 64;
+  while (l > 1 && (pieces % l)) l >>= 1;
+  return l;
+}
+
+MOE_DEV float group_sum_dyn(float v, int lpr) {
+  for (int off = lpr / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,275 @@
+// Router, top-k, grouping, combine and dequantisation kernels (gfx950).
+//
+// The layer routes every token to the k best of E experts through a "fused
+// top-k router", groups the (token, expert) pairs for "expert-indexed GEMVs"
+// or a grouped GEMM ("[Model] Add Flint (RecursiveSI/flint)", section "What
+// happened"), and adds the weighted expert outputs to an always-on shared
+// expert ("Recursive Flint: 125 tok/s on an M4 Pro, measured where it matters
+// least", table under "What actually shipped").
+#include "common.cuh"
+#include "launch.h"
+#include "route.cuh"
+
+namespace moe {
+
+// ---------------------------------------------------------------- dequant
+// One thread per 8 consecutive elements (one 32-bit word of codes); the
+// tensor scale of the expert is read from device memory.
+__global__ void __launch_bounds__(256) k_dequant_dev_ts(int fmt, int rows, int cols, const uint8_t* __restrict__ codes,
+                                                        const void* __restrict__ scales,
+                                                        const uint8_t* __restrict__ zeros,
+                                                        const float* __restrict__ ts_ptr, float* __restrict__ out) {
+  const float ts = (fmt == kFmtNvfp4) ? *ts_ptr : 1.0f;
+  const int words_per_row = cols / 8;
+  const long long w = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= (long long)rows * words_per_row) return;
+  const int r = (int)(w / words_per_row);
+  const int c0 = (int)(w % words_per_row) * 8;
+  const uint32_t word = *(const uint32_t*)(codes + (size_t)r * (cols / 2) + c0 / 2);
+  float v[8];
+  if (fmt == kFmtNvfp4) {
+    const uint8_t sb = ((const uint8_t*)scales)[(size_t)r * (cols / 16) + c0 / 16];
+    const float b = e4m3_to_f32(sb, 0);
+    moe_f32x2 p0 = e2m1x2_to_f32<0>(word), p1 = e2m1x2_to_f32<1>(word);
+    moe_f32x2 p2 = e2m1x2_to_f32<2>(word), p3 = e2m1x2_to_f32<3>(word);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+    v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (b * v[i]) * ts;
+  } else {
+    const size_t g = (size_t)r * (cols / 64) + c0 / 64;
+    const float s = f16_to_f32(((const uint16_t*)scales)[g]);
+    const int z = zeros[g];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s * (float)((int)((word >> (4 * i)) & 15u) - z);
+  }
+  float4* o = (float4*)(out + (size_t)r * cols + c0);
+  o[0] = make_float4(v[0], v[1], v[2], v[3]);
+  o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* codes, const void* scales,
+                                 const uint8_t* zeros, const float* ts_dev, float* out, hipStream_t s) {
+  const long long words = (long long)rows * (cols / 8);
+  const int blocks = (int)((words + 255) / 256);
+  hipLaunchKernelGGL(k_dequant_dev_ts, dim3(blocks), dim3(256), 0, s, fmt, rows, cols, codes, scales, zeros, ts_dev,
+                     out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- router GEMV
+// logits[t, e] = sum_h x[t, h] * w_router[e, h], fp32 accumulation.
+// Block: 4 waves = 4 experts; up to kRouteTok tokens staged in LDS as bf16.
+constexpr int kRouteTok = 8;
+
+__global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                       int T, int H, int E, int tpb, float* __restrict__ logits) {
+  extern __shared__ uint16_t xs[];  // [tpb][H], tpb <= kRouteTok
+  const int t0 = blockIdx.y * tpb;
+  const int nt = min(tpb, T - t0);
+  // stage tokens: 8 bytes per thread-step
+  for (int i = threadIdx.x; i < nt * H / 4; i += blockDim.x) {
+    const int t = i / (H / 4), c = i % (H / 4);
+    ((uint2*)xs)[t * (H / 4) + c] = ((const uint2*)(x + (size_t)(t0 + t) * H))[c];
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  float acc[kRouteTok];
+#pragma unroll
+  for (int t = 0; t < kRouteTok; ++t) acc[t] = 0.f;
+  const float4* wrow = (const float4*)(wr + (size_t)e * H);
+  for (int c = lane; c < H / 4; c += 64) {
+    const float4 w = wrow[c];
+#pragma unroll
+    for (int t = 0; t < kRouteTok; ++t) {
+      if (t < nt) {
+        const uint2 xv = ((const uint2*)xs)[t * (H / 4) + c];
+        float a = acc[t];
+        a = fmaf(w.x, bf16_to_f32(xv.x & 0xffffu), a);
+        a = fmaf(w.y, bf16_to_f32(xv.x >> 16), a);
+        a = fmaf(w.z, bf16_to_f32(xv.y & 0xffffu), a);
+        a = fmaf(w.w, bf16_to_f32(xv.y >> 16), a);
+        acc[t] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouteTok; ++t) {
+    if (t < nt) {
+      const float v = group_sum<64>(acc[t]);
+      if (lane == 0) logits[(size_t)(t0 + t) * E + e] = v;
+    }
+  }
+}
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
+                                hipStream_t s) {
+  const int tpb = std::max(1, std::min(kRouteTok, 16384 / H));  // <= 32 KB of LDS
+  dim3 grid((E + 3) / 4, (T + tpb - 1) / tpb);
+  const size_t lds = (size_t)tpb * H * sizeof(uint16_t);
+  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), lds, s, x, wr, T, H, E, tpb, logits);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- top-k + softmax
+__global__ void __launch_bounds__(256) k_topk_softmax(const float* __restrict__ logits, int T, int E, int k,
+                                                      int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  wave_topk_softmax(logits + (size_t)t * E, E, k, threadIdx.x & 63, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- permute
+// Stable counting sort of pairs p = t*k + j by expert id, in chunks of
+// kPermChunk pairs: per-chunk histograms, one scan, per-chunk scatter.
+constexpr int kPermChunk = 256;
+
+__global__ void __launch_bounds__(256) k_perm_hist(const int32_t* __restrict__ ids, int n, int E,
+                                                   int32_t* __restrict__ hist) {
+  extern __shared__ int32_t h[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kPermChunk + threadIdx.x;
+  if (p < n) atomicAdd(&h[ids[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block (1024 threads): per-expert totals, exclusive scan, per-chunk bases.
+__global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[1024];
+  __shared__ int32_t scan[1025];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = run;  // exclusive within the expert
+      run += v;
+    }
+  }
+  tot[e] = (e < E) ? run : 0;
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+      scan[i] = acc;
+      acc += tot[i];
+    }
+    scan[E] = acc;
+  }
+  __syncthreads();
+  if (e < E) {
+    counts[e] = tot[e];
+    offsets[e] = scan[e];
+    for (int c = 0; c < nchunks; ++c) hist[(size_t)c * E + e] += scan[e];
+  }
+  if (e == 0) offsets[E] = scan[E];
+}
+
+__global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ sorted_pairs,
+                                                      int32_t* __restrict__ pair_pos) {
+  __shared__ int32_t cid[kPermChunk];
+  const int p0 = blockIdx.x * kPermChunk;
+  const int i = threadIdx.x;
+  const int p = p0 + i;
+  cid[i] = (p < n) ? ids[p] : -1;
+  __syncthreads();
+  if (p >= n) return;
+  const int e = cid[i];
+  int rank = 0;
+  for (int q = 0; q < i; ++q) rank += (cid[q] == e);
+  const int pos = base[(size_t)blockIdx.x * E + e] + rank;
+  sorted_pairs[pos] = p;
+  pair_pos[p] = pos;
+}
+
+// x_perm[r] = x[sorted_pairs[r] / k]; one block per row, 16 bytes per thread-step.
+__global__ void __launch_bounds__(256) k_gather_rows(const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ sorted_pairs, int k, int H,
+                                                     uint16_t* __restrict__ x_perm) {
+  const int r = blockIdx.x;
+  const int t = sorted_pairs[r] / k;
+  const uint4* src = (const uint4*)(x + (size_t)t * H);
+  uint4* dst = (uint4*)(x_perm + (size_t)r * H);
+  for (int c = threadIdx.x; c < H / 8; c += blockDim.x) dst[c] = src[c];
+}
+
+size_t permute_ws_bytes(int T, int k, int E) {
+  const long long n = (long long)T * k;
+  const long long nchunks = (n + kPermChunk - 1) / kPermChunk;
+  return (size_t)(nchunks * E * sizeof(int32_t));
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, const uint16_t* x, uint16_t* x_perm, int H,
+                          void* ws, hipStream_t s) {
+  const int n = T * k;
+  const int nchunks = (n + kPermChunk - 1) / kPermChunk;
+  int32_t* hist = (int32_t*)ws;
+  hipLaunchKernelGGL(k_perm_hist, dim3(nchunks), dim3(kPermChunk), E * sizeof(int32_t), s, ids, n, E, hist);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, nchunks, E, hist, counts, offsets);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, hist, sorted_pairs, pair_pos);
+  if (x && x_perm) hipLaunchKernelGGL(k_gather_rows, dim3(n), dim3(256), 0, s, x, sorted_pairs, k, H, x_perm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine
+// y[t] = residual[t] + sum_j w[t,j] * out_perm[pair_pos[t*k+j]] + out_shared[t];
+// accumulation order: slots 0..k-1, then shared, then residual.
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ out_perm,
+                                                 const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
+                                                 const float* __restrict__ out_shared,
+                                                 const uint16_t* __restrict__ residual, int k, int H,
+                                                 uint16_t* __restrict__ y, float* __restrict__ y_f32) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // group of 4 elements
+  if (c * 4 >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const float4 o = ((const float4*)(out_perm + (size_t)pair_pos[(size_t)t * k + j] * H))[c];
+    acc.x = fmaf(wj, o.x, acc.x);
+    acc.y = fmaf(wj, o.y, acc.y);
+    acc.z = fmaf(wj, o.z, acc.z);
+    acc.w = fmaf(wj, o.w, acc.w);
+  }
+  if (out_shared) {
+    const float4 o = ((const float4*)(out_shared + (size_t)t * H))[c];
+    acc.x += o.x;
+    acc.y += o.y;
+    acc.z += o.z;
+    acc.w += o.w;
+  }
+  if (residual) {
+    const uint2 r = ((const uint2*)(residual + (size_t)t * H))[c];
+    acc.x += bf16_to_f32(r.x & 0xffffu);
+    acc.y += bf16_to_f32(r.x >> 16);
+    acc.z += bf16_to_f32(r.y & 0xffffu);
+    acc.w += bf16_to_f32(r.y >> 16);
+  }
+  uint2 o;
+  o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+  o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+  ((uint2*)(y + (size_t)t * H))[c] = o;
+  if (y_f32) ((float4*)(y_f32 + (size_t)t * H))[c] = acc;
+}
+
+hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const float* w, const float* out_shared,
+                          const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s) {
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, out_perm, pair_pos, w, out_shared, residual, k, H, y, y_f32);
+  return hipGetLastError();
+}
+
+}  // namespace moe

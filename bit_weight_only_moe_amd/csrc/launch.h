@@ -1,0 +1,34 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/moe_w4a16.h"
+
+namespace moe {
+
+hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* codes, const void* scales,
+                                 const uint8_t* zeros, const float* ts_dev, float* out, hipStream_t s);
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
+                                hipStream_t s);
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+size_t permute_ws_bytes(int T, int k, int E);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, const uint16_t* x, uint16_t* x_perm, int H,
+                          void* ws, hipStream_t s);
+hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const float* w, const float* out_shared,
+                          const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s);
+hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, hipStream_t s);
+hipError_t launch_gemv_ffn(const moe_ffn_weights* routed, const int32_t* active, const int32_t* offsets,
+                           const int32_t* sorted_pairs, int k, int max_active, const moe_ffn_weights* shared,
+                           int shared_T, const uint16_t* x, int H, uint16_t* h_routed, uint16_t* h_shared,
+                           float* out_routed, float* out_shared, hipStream_t s);
+hipError_t launch_decode_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                               int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active, int32_t* ids_out,
+                               float* w_out, hipStream_t s);
+
+}  // namespace moe

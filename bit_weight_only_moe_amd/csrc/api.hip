@@ -96,6 +96,7 @@ size_t grouped_ws(int E, int I, int total_rows, Carve* c, int32_t** active, uint
 }
 
 struct DecodeWs {
+  int* sync;
   float* logits;
   int32_t* ids;
   float* w;
@@ -116,6 +117,7 @@ size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
   const int Is = L->shared ? L->shared->gate.rows : 0;
   const size_t n = (size_t)T * L->k;
   DecodeWs t;
+  t.sync = c.take<int>((size_t)moe::layer_decode_sync_words(L->H));
   t.logits = c.take<float>((size_t)T * L->E);
   t.ids = c.take<int32_t>(n);
   t.w = c.take<float>(n);
@@ -128,7 +130,7 @@ size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
   t.h_shared = c.take<uint16_t>((size_t)T * Is);
   t.o_routed = c.take<float>(n * L->H);
   t.o_shared = c.take<float>((size_t)T * L->H);
-  t.perm_ws = c.take<char>(T > kDecodeMaxT ? moe::permute_ws_bytes(T, L->k, L->E) : 0);
+  t.perm_ws = c.take<char>(moe::permute_ws_bytes(T, L->k, L->E));
   if (d) *d = t;
   return c.used;
 }
@@ -252,8 +254,8 @@ int moe_grouped_w4a16_ffn(const moe_ffn_weights* w, int E, int H, int I, const u
   hipStream_t s = as_stream(stream);
   hipError_t e = moe::launch_active_list(offsets, E, active, s);
   if (e == hipSuccess)
-    e = moe::launch_gemv_ffn(w, active, offsets, sorted_pairs, k, std::min(E, total_rows), nullptr, 0, x, H, h,
-                             nullptr, out, nullptr, s);
+    e = moe::launch_grouped_gemv(w, active, offsets, sorted_pairs, k, std::min(E, total_rows), x, H, I, h, out,
+                                 total_rows, s);
   return hip_status(e, "moe_grouped_w4a16_ffn");
 }
 
@@ -312,25 +314,29 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
   decode_ws(L, T, ws, &d);
   hipStream_t s = as_stream(stream);
   const int E = L->E, k = L->k, H = L->H;
+  const int Is = L->shared ? L->shared->gate.rows : 0;
+  if (moe::layer_decode_lds(T, H, L->I, Is, E, k) > 0)
+    return hip_status(moe::launch_layer_decode(L, x, residual, T, y, d.sync, d.logits, d.ids, d.w, d.offsets,
+                                               d.sorted_pairs, d.pair_pos, d.active, d.h_routed, d.h_shared,
+                                               d.o_routed, d.o_shared, ids_out, w_out, s),
+                      "moe_layer_decode");
+  // Larger batches: composed from the separate kernels (route, group, routed experts, the shared expert as
+  // one unit, combine).
   hipError_t e = moe::launch_router_logits(x, L->w_router, T, H, E, d.logits, s);
-  if (e != hipSuccess) return hip_status(e, "moe_layer_decode");
-  if (T <= kDecodeMaxT) {
-    e = moe::launch_decode_route(d.logits, T, E, k, d.ids, d.w, d.offsets, d.sorted_pairs, d.pair_pos, d.active,
-                                 ids_out, w_out, s);
-  } else {
-    e = moe::launch_topk_softmax(d.logits, T, E, k, d.ids, d.w, s);
-    if (e == hipSuccess)
-      e = moe::launch_permute(d.ids, T, k, E, d.counts, d.offsets, d.sorted_pairs, d.pair_pos,
-                              nullptr, nullptr, H, d.perm_ws, s);
-    if (e == hipSuccess) e = moe::launch_active_list(d.offsets, E, d.active, s);
-    if (e == hipSuccess && ids_out) {
-      e = hipMemcpyAsync(ids_out, d.ids, sizeof(int32_t) * T * k, hipMemcpyDeviceToDevice, s);
-      if (e == hipSuccess) e = hipMemcpyAsync(w_out, d.w, sizeof(float) * T * k, hipMemcpyDeviceToDevice, s);
-    }
+  if (e == hipSuccess) e = moe::launch_topk_softmax(d.logits, T, E, k, d.ids, d.w, s);
+  if (e == hipSuccess)
+    e = moe::launch_permute(d.ids, T, k, E, d.counts, d.offsets, d.sorted_pairs, d.pair_pos, nullptr, nullptr, H,
+                            d.perm_ws, s);
+  if (e == hipSuccess) e = moe::launch_active_list(d.offsets, E, d.active, s);
+  if (e == hipSuccess && ids_out) {
+    e = hipMemcpyAsync(ids_out, d.ids, sizeof(int32_t) * T * k, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(w_out, d.w, sizeof(float) * T * k, hipMemcpyDeviceToDevice, s);
   }
   if (e == hipSuccess)
-    e = moe::launch_gemv_ffn(&L->experts, d.active, d.offsets, d.sorted_pairs, k, std::min(E, T * k), L->shared, T,
-                             x, H, d.h_routed, d.h_shared, d.o_routed, d.o_shared, s);
+    e = moe::launch_grouped_gemv(&L->experts, d.active, d.offsets, d.sorted_pairs, k, std::min(E, T * k), x, H,
+                                 L->I, d.h_routed, d.o_routed, T * k, s);
+  if (e == hipSuccess && L->shared)
+    e = moe::launch_grouped_gemv(L->shared, nullptr, nullptr, nullptr, 1, 1, x, H, Is, d.h_shared, d.o_shared, T, s);
   if (e == hipSuccess)
     e = moe::launch_combine(d.o_routed, d.pair_pos, d.w, L->shared ? d.o_shared : nullptr, residual, T, k, H, y,
                             nullptr, s);

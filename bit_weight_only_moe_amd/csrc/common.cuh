@@ -83,3 +83,134 @@ MOE_DEV float group_sum(float v) {
 MOE_DEV uint32_t ld_nc_u32(const void* p) { return __builtin_nontemporal_load((const uint32_t*)p); }
 
 }  // namespace moe
+
+namespace moe {
+
+// ---- DPP-based wave reductions (gfx9 row_shr / row_bcast) ---------------
+// Each helper leaves the full result in every lane.
+
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+MOE_DEV uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+MOE_DEV uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+MOE_DEV uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BANK_MASK>(0u, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BANK_MASK>(0u, (uint32_t)(v >> 32));
+  return max_u64(v, ((uint64_t)hi << 32) | lo);
+}
+
+// Maximum of a 64-bit key over the wave (0 is the identity): inclusive
+// max-scan with row_shr 1, 2, 3, 4, 8 and row_bcast 15, 31; lane 63 holds
+// the result, which is broadcast to all lanes.
+MOE_DEV uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0x111, 0xf, 0xf>(v);
+  v = dpp_max_step<0x112, 0xf, 0xf>(v);
+  v = dpp_max_step<0x113, 0xf, 0xf>(v);
+  v = dpp_max_step<0x114, 0xf, 0xe>(v);
+  v = dpp_max_step<0x118, 0xf, 0xc>(v);
+  v = dpp_max_step<0x142, 0xa, 0xf>(v);
+  v = dpp_max_step<0x143, 0xc, 0xf>(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// fp32 -> uint32 whose unsigned order is the numeric order (-0 folded onto +0).
+MOE_DEV uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ---- workgroup / device synchronisation ---------------------------------
+MOE_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---- device-coherent accesses for data exchanged between blocks ---------
+// Agent-scope relaxed atomic loads/stores are coherent across the chip's
+// separate L2 caches without the cache write-back / invalidate that an
+// agent-scope fence implies.  A producer stores with st_dev, waits for its
+// stores to complete (workgroup-scope release), then bumps a counter; a
+// consumer polls the counter and then reads with ld_dev.
+MOE_DEV void st_dev(int32_t* p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MOE_DEV void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV void st_dev(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV float ld_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load((uint32_t*)const_cast<float*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+MOE_DEV uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---- DPP group sums ------------------------------------------------------
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+MOE_DEV float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                               BANK_MASK, false));
+}
+
+// Sum over each group of G consecutive lanes (G a power of two <= 64); the
+// total lands in the LAST lane of each group (other lanes hold partial sums).
+// Built from row_shr (within 16-lane rows) and row_bcast (across rows).
+template <int G>
+MOE_DEV float group_sum_last(float x) {
+  float v = x;
+  if (G == 2) {
+    v = x + dpp_f32<0x111, 0xf, 0xf>(x);
+  } else if (G >= 4) {
+    v = x + dpp_f32<0x111, 0xf, 0xf>(x) + dpp_f32<0x112, 0xf, 0xf>(x) + dpp_f32<0x113, 0xf, 0xf>(x);
+  }
+  if (G >= 8) v += dpp_f32<0x114, 0xf, 0xa>(v);
+  if (G >= 16) v += dpp_f32<0x118, 0xf, 0xc>(v);
+  if (G >= 32) v += dpp_f32<0x142, 0xa, 0xf>(v);
+  if (G >= 64) v += dpp_f32<0x143, 0xc, 0xf>(v);
+  return v;
+}
+
+MOE_DEV float group_sum_last_dyn(float v, int g) {
+  switch (g) {
+    case 64: return group_sum_last<64>(v);
+    case 32: return group_sum_last<32>(v);
+    case 16: return group_sum_last<16>(v);
+    case 8: return group_sum_last<8>(v);
+    case 4: return group_sum_last<4>(v);
+    case 2: return group_sum_last<2>(v);
+    default: return v;
+  }
+}
+
+// Full-wave sum broadcast to every lane.
+MOE_DEV float wave_sum(float v) {
+  v = group_sum_last<64>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+}  // namespace moe

@@ -21,9 +21,17 @@
 
 namespace moe {
 
+template <bool COH>
+MOE_DEV uint4 load16(const uint4* p) {
+  if (!COH) return *p;
+  const uint64_t a = ld_dev((const uint64_t*)p), b = ld_dev((const uint64_t*)p + 1);
+  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+
 // Stage one token row (K bf16 values from global) into LDS in the FMT layout.
-// Thread `tid` of `nthr` handles whole 32-element pieces.
-template <int FMT>
+// Thread `tid` of `nthr` handles whole 32-element pieces.  COH: the row was
+// written by another block of the same launch (device-coherent loads).
+template <int FMT, bool COH = false>
 MOE_DEV void stage_token(uint16_t* __restrict__ dst, float* __restrict__ dsum, const uint16_t* __restrict__ src,
                          int K, int tid, int nthr) {
   const int npieces = K / 32;
@@ -32,12 +40,12 @@ MOE_DEV void stage_token(uint16_t* __restrict__ dst, float* __restrict__ dsum, c
     uint4* d = (uint4*)(dst + 32 * p);
     if (FMT == kFmtNvfp4) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) d[c] = s[c];
+      for (int c = 0; c < 4; ++c) d[c] = load16<COH>(s + c);
     } else {
       float sum = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 v = s[c];
+        const uint4 v = load16<COH>(s + c);
         // elements 0..7 as 16-bit halves of v.x .. v.w
         const uint32_t e0 = v.x & 0xffffu, e1 = v.x >> 16, e2 = v.y & 0xffffu, e3 = v.y >> 16;
         const uint32_t e4 = v.z & 0xffffu, e5 = v.z >> 16, e6 = v.w & 0xffffu, e7 = v.w >> 16;

@@ -98,8 +98,8 @@ __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restric
 #pragma unroll
   for (int t = 0; t < kRouteTok; ++t) {
     if (t < nt) {
-      const float v = group_sum<64>(acc[t]);
-      if (lane == 0) logits[(size_t)(t0 + t) * E + e] = v;
+      const float v = group_sum_last<64>(acc[t]);  // same reduction order as the fused decode router
+      if (lane == 63) logits[(size_t)(t0 + t) * E + e] = v;
     }
   }
 }
@@ -269,6 +269,24 @@ hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const 
                           const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
   hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, out_perm, pair_pos, w, out_shared, residual, k, H, y, y_f32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- active experts
+// active[0] = number of experts with rows, active[1 + a] = their ids (increasing).
+__global__ void __launch_bounds__(1024) k_active_list(const int32_t* __restrict__ offsets, int E,
+                                                      int32_t* __restrict__ active) {
+  __shared__ int scan_lds[17];
+  const int e = threadIdx.x;
+  const int flag = (e < E) && (offsets[e + 1] > offsets[e]);
+  int total;
+  const int pos = block_exclusive_scan(flag, scan_lds, total);
+  if (flag) active[1 + pos] = e;
+  if (e == 0) active[0] = total;
+}
+
+hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, hipStream_t s) {
+  hipLaunchKernelGGL(k_active_list, dim3(1), dim3(1024), 0, s, offsets, E, active);
   return hipGetLastError();
 }
 

@@ -23,12 +23,16 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
 hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const float* w, const float* out_shared,
                           const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s);
 hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, hipStream_t s);
-hipError_t launch_gemv_ffn(const moe_ffn_weights* routed, const int32_t* active, const int32_t* offsets,
-                           const int32_t* sorted_pairs, int k, int max_active, const moe_ffn_weights* shared,
-                           int shared_T, const uint16_t* x, int H, uint16_t* h_routed, uint16_t* h_shared,
-                           float* out_routed, float* out_shared, hipStream_t s);
-hipError_t launch_decode_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
-                               int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active, int32_t* ids_out,
-                               float* w_out, hipStream_t s);
+hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, const int32_t* offsets,
+                               const int32_t* sorted_pairs, int k, int max_active, const uint16_t* x, int H, int I,
+                               uint16_t* h, float* out, int rows, hipStream_t s);
+
+size_t layer_decode_lds(int T, int H, int I, int Is, int E, int k);
+int layer_decode_sync_words(int H);
+hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
+                               uint16_t* y, int* sync, float* logits, int32_t* ids, float* w, int32_t* offsets,
+                               int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active, uint16_t* h_routed,
+                               uint16_t* h_shared, float* o_routed, float* o_shared, int32_t* ids_out, float* w_out,
+                               hipStream_t s);
 
 }  // namespace moe

@@ -226,9 +226,14 @@ def run_layer(layer, x, residual, T):
     w = torch.empty((T, layer["k"]), dtype=torch.float32, device=DEV)
     L = moe.Layer(layer)
     nws = moe.moe_layer_decode_workspace_size(L, T)
-    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=DEV)
     moe.moe_layer_decode(L, x, residual, T, y, ids, w, ws, nws)
+    moe.moe_layer_decode(L, x, residual, T, y, ids, w, ws, nws)   # the workspace is reusable as left
     sync()
+    H = layer["H"]
+    words = ws[:64 * (2 + H // 64)].view(torch.int32).cpu().numpy()
+    tickets = np.concatenate([words[:1], words[16::16][: (H + 63) // 64]])
+    assert not tickets.any(), tickets   # every ticket counter left reset for the next call
     return y, ids, w
 
 
@@ -347,7 +352,7 @@ def test_layer_decode_graph_capture_replays():
     x = synth.make_tokens(T, H, 90, DEV)
     L = moe.Layer(layer)
     nws = moe.moe_layer_decode_workspace_size(L, T)
-    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=DEV)
     y_eager = torch.empty_like(x)
     moe.moe_layer_decode(L, x, x, T, y_eager, None, None, ws, nws)
     sync()

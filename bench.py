@@ -56,6 +56,10 @@ def main():
     dev = "cuda"
     fmt = synth.FMT_NAMES[args.fmt]
     workload = args.workload
+    if workload == "prefill":
+        return bench_prefill(args, fmt)
+    if workload == "chain_b8":
+        return bench_chain(args, fmt)
     T = {"decode_b1": 1, "decode_T4": 4, "decode_T16": 16, "decode_T64": 64}.get(workload)
     if T is None:
         print("unknown workload %s" % workload, file=sys.stderr)
@@ -175,6 +179,136 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def timed_graph(torch, stream, body, K, W):
+    """Warm up W eager steps, capture K steps in one graph, time one replay."""
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            body(i, stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(K):
+            body(i, stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)
+
+
+def bench_prefill(args, fmt):
+    """4096-token prefill of one Flint-shaped layer with Zipf(1.1) expert popularity."""
+    import torch
+    import bit_weight_only_moe_amd as moe
+    import synth
+    dev = "cuda"
+    H, I, E, k, T = 2048, 768, 256, 6, 4096
+    R = max(1, min(args.copies, 2))
+    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(5, r), dev) for r in range(R)]
+    x = synth.make_tokens(T, H, 5, dev)
+    zl = synth.zipf_logits(T, E, 1.1, 5, dev)
+    n = T * k
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(n, dtype=torch.int32, device=dev)
+    pp = torch.empty(n, dtype=torch.int32, device=dev)
+    pws_n = moe.moe_permute_workspace_size(T, k, E)
+    pws = torch.empty(pws_n, dtype=torch.uint8, device=dev)
+    out = torch.empty((n, H), dtype=torch.float32, device=dev)
+    out_s = torch.empty((T, H), dtype=torch.float32, device=dev)
+    off_s = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    gws_n = max(moe.moe_grouped_ffn_workspace_size(E, H, I, n), moe.moe_grouped_ffn_workspace_size(1, H, I, T))
+    gws = torch.empty(gws_n, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    f_routed = [moe.ffn_weights(l["experts"]) for l in layers]
+    f_shared = [moe.ffn_weights(l["shared"]) for l in layers]
+
+    def step(i, s):
+        L = layers[i % R]
+        moe.moe_route(x, L["w_router"], T, H, E, k, lg, ids, w, stream=s)   # router GEMM (timed; skewed logits route)
+        moe.moe_topk_softmax(zl, T, E, k, ids, w, stream=s)
+        moe.moe_permute(ids, T, k, E, counts, offsets, sp, pp, None, None, 0, pws, pws_n, stream=s)
+        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
+                                  gws_n, stream=s)
+        moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws,
+                                  gws_n, stream=s)
+        moe.moe_combine(out, pp, w, out_s, x, T, k, H, y, stream=s)
+
+    stream = torch.cuda.Stream()
+    ms = timed_graph(torch, stream, step, K, W)
+    # the grouped FFN alone (routed + shared), timed the same way
+    def ffn_only(i, s):
+        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
+                                  gws_n, stream=s)
+        moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws,
+                                  gws_n, stream=s)
+    ms_ffn = timed_graph(torch, stream, ffn_only, K, W)
+    flops = 6.0 * (n + T) * H * I
+    c = counts.cpu().numpy()
+    out_line = {
+        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
+        "value": flops / (ms / K * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "w4(%s)/bf16 mfma/fp32 acc" % args.fmt, "data": "synthetic",
+        "config": {"workload": "moe_prefill T=4096 %s H=2048 I=768 E=256 top6+1shared zipf1.1" % args.fmt,
+                   "expert_gflop": flops / 1e9, "tokens_per_s": T * K / (ms * 1e-3),
+                   "max_rows_per_expert": int(c.max()), "min_rows_per_expert": int(c.min()), "weight_copies": R},
+        "roofline": {"bound": "mfma", "achieved": flops / (ms_ffn / K * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (ms_ffn / K * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "moe_grouped_w4a16_ffn (routed + shared, MFMA)"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out_line))
+
+
+def bench_chain(args, fmt):
+    """One decode step through 47 chained MoE layers at batch 8, residual add between layers."""
+    import torch
+    import bit_weight_only_moe_amd as moe
+    import synth
+    dev = "cuda"
+    H, I, E, k, T, NL = 2048, 768, 256, 6, 8, 47
+    K, W = max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
+    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(4, l), dev) for l in range(NL)]
+    Ls = [moe.Layer(l) for l in layers]
+    xs = [synth.make_tokens(T, H, 4, dev)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    ids = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NL)]
+    ws_ = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NL)]
+    nws = moe.moe_layer_decode_workspace_size(Ls[0], T)
+    wsb = torch.zeros(nws, dtype=torch.uint8, device=dev)
+
+    def step(i, s):
+        for l in range(NL):
+            moe.moe_layer_decode(Ls[l], xs[l], xs[l], T, xs[l + 1], ids[l], ws_[l], wsb, nws, stream=s)
+
+    stream = torch.cuda.Stream()
+    ms = timed_graph(torch, stream, step, K, W)
+    eb = synth.expert_bytes(fmt, H, I)
+    bytes_step = sum((len(np.unique(ids[l].cpu().numpy())) + 1) * eb for l in range(NL))
+    gbs = bytes_step / (ms / K * 1e-3) / 1e9
+    out_line = {
+        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
+        "value": T * K / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "w4(%s)/bf16 act/fp32 acc" % args.fmt, "data": "synthetic",
+        "config": {"workload": "moe_decode_chain 47 layers T=8 %s H=2048 I=768 E=256 top6+1shared" % args.fmt,
+                   "expert_bytes_per_step": bytes_step, "resident_weight_bytes": NL * (E + 1) * eb},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "47 x moe_layer_decode"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out_line))
 
 
 if __name__ == "__main__":

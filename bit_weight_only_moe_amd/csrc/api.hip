@@ -110,6 +110,7 @@ struct DecodeWs {
   float* o_routed;
   float* o_shared;
   void* perm_ws;
+  void* mfma_ws;
 };
 
 size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
@@ -131,6 +132,9 @@ size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
   t.o_routed = c.take<float>(n * L->H);
   t.o_shared = c.take<float>((size_t)T * L->H);
   t.perm_ws = c.take<char>(moe::permute_ws_bytes(T, L->k, L->E));
+  t.mfma_ws = c.take<char>(T > kDecodeMaxT ? std::max(moe::mfma_ws_bytes(L->E, L->H, L->I, (int)n),
+                                                      moe::mfma_ws_bytes(1, L->H, Is, T))
+                                           : 0);
   if (d) *d = t;
   return c.used;
 }
@@ -219,11 +223,20 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
                     "moe_permute");
 }
 
+// MFMA when the average expert gets enough rows to fill matrix-core tiles.
+constexpr int kAutoMfmaRowsPerExpert = 16;
+
+static bool use_mfma(int mode, int E, int H, int I, int total_rows) {
+  if (mode == MOE_MODE_MFMA) return true;
+  if (mode == MOE_MODE_GEMV) return false;
+  return moe::mfma_shape_ok(H, I) && total_rows >= kAutoMfmaRowsPerExpert * E;
+}
+
 size_t moe_grouped_ffn_workspace_size(int E, int H, int I, int total_rows, int mode) {
-  (void)H;
-  (void)mode;
-  if (E < 1 || I < 1 || total_rows < 0) return 0;
-  return grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
+  if (E < 1 || I < 1 || H < 1 || total_rows < 0) return 0;
+  const size_t gemv = grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
+  if (mode == MOE_MODE_GEMV) return gemv;
+  return std::max(gemv, moe::mfma_ws_bytes(E, H, I, total_rows));
 }
 
 int moe_grouped_w4a16_ffn(const moe_ffn_weights* w, int E, int H, int I, const uint16_t* x,
@@ -241,12 +254,18 @@ int moe_grouped_w4a16_ffn(const moe_ffn_weights* w, int E, int H, int I, const u
   int rc = check_ffn(*w, "moe_grouped_w4a16_ffn.w", E, H, I);
   if (rc) return rc;
   if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: x/out alignment");
-  const size_t need = grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
-  if (!ws || ws_bytes < need)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: workspace %zu < %zu bytes", ws_bytes, need);
-  if (mode == MOE_MODE_MFMA)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: MFMA mode not available in this build");
+  const bool mfma = use_mfma(mode, E, H, I, total_rows);
+  if (mfma && !moe::mfma_shape_ok(H, I))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: MFMA mode needs H %% 128 == 0 (H=%d)", H);
+  const size_t need = mfma ? moe::mfma_ws_bytes(E, H, I, total_rows) : grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: workspace %zu < %zu bytes or not 256-byte aligned",
+                ws_bytes, need);
   if (total_rows == 0) return MOE_OK;
+  if (mfma)
+    return hip_status(moe::launch_grouped_mfma(w, E, offsets, sorted_pairs, k, x, H, I, total_rows, out, ws,
+                                               as_stream(stream)),
+                      "moe_grouped_w4a16_ffn");
   Carve c(ws);
   int32_t* active;
   uint16_t* h;
@@ -332,11 +351,21 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
     e = hipMemcpyAsync(ids_out, d.ids, sizeof(int32_t) * T * k, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(w_out, d.w, sizeof(float) * T * k, hipMemcpyDeviceToDevice, s);
   }
-  if (e == hipSuccess)
-    e = moe::launch_grouped_gemv(&L->experts, d.active, d.offsets, d.sorted_pairs, k, std::min(E, T * k), x, H,
-                                 L->I, d.h_routed, d.o_routed, T * k, s);
-  if (e == hipSuccess && L->shared)
-    e = moe::launch_grouped_gemv(L->shared, nullptr, nullptr, nullptr, 1, 1, x, H, Is, d.h_shared, d.o_shared, T, s);
+  if (e == hipSuccess) {
+    if (use_mfma(MOE_MODE_AUTO, E, H, L->I, T * k))
+      e = moe::launch_grouped_mfma(&L->experts, E, d.offsets, d.sorted_pairs, k, x, H, L->I, T * k, d.o_routed,
+                                   d.mfma_ws, s);
+    else
+      e = moe::launch_grouped_gemv(&L->experts, d.active, d.offsets, d.sorted_pairs, k, std::min(E, T * k), x, H,
+                                   L->I, d.h_routed, d.o_routed, T * k, s);
+  }
+  if (e == hipSuccess && L->shared) {
+    if (use_mfma(MOE_MODE_AUTO, 1, H, Is, T))
+      e = moe::launch_grouped_mfma(L->shared, 1, nullptr, nullptr, 1, x, H, Is, T, d.o_shared, d.mfma_ws, s);
+    else
+      e = moe::launch_grouped_gemv(L->shared, nullptr, nullptr, nullptr, 1, 1, x, H, Is, d.h_shared, d.o_shared, T,
+                                   s);
+  }
   if (e == hipSuccess)
     e = moe::launch_combine(d.o_routed, d.pair_pos, d.w, L->shared ? d.o_shared : nullptr, residual, T, k, H, y,
                             nullptr, s);

@@ -35,4 +35,10 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
                                uint16_t* h_shared, float* o_routed, float* o_shared, int32_t* ids_out, float* w_out,
                                hipStream_t s);
 
+size_t mfma_ws_bytes(int E, int H, int I, int total_rows);
+bool mfma_shape_ok(int H, int I);
+hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* offsets, const int32_t* sorted_pairs,
+                               int k, const uint16_t* x, int H, int I, int total_rows, float* out, void* ws,
+                               hipStream_t s);
+
 }  // namespace moe

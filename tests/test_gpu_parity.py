@@ -373,3 +373,119 @@ def test_layer_decode_graph_capture_replays():
         sync()
         assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), rep
         del junk
+
+
+# ------------------------------------------------------------------ MFMA grouped FFN (prefill / large batch)
+
+MFMA_CASES = [
+    # fmt, H, I, E, k, T, seed, routing
+    (2, 256, 128, 32, 6, 64, 100, "uniform"),
+    (1, 256, 192, 8, 3, 300, 101, "zipf"),       # several 128-row tiles per expert, ragged tails
+    (1, 2048, 768, 256, 6, 512, 102, "zipf"),
+    (2, 2048, 768, 256, 6, 512, 103, "zipf"),
+]
+
+
+def routed_rows(T, E, k, seed, routing):
+    lg = (synth.zipf_logits(T, E, 1.1, seed, "cpu") if routing == "zipf" else synth.uniform_logits(T, E, seed, "cpu"))
+    ids = oracle.topk_select(lg.numpy().astype(np.float64), k)
+    return ids, oracle.permute(ids, E)
+
+
+@pytest.mark.parametrize("fmt,H,I,E,k,T,seed,routing", MFMA_CASES)
+def test_grouped_ffn_mfma(fmt, H, I, E, k, T, seed, routing):
+    print("grouped_ffn mfma", fmt, H, I, E, k, T, seed, routing, flush=True)
+    layer = synth.make_layer(fmt, H, I, E, k, seed, DEV)
+    x = synth.make_tokens(T, H, seed, DEV)
+    ids, (counts, offsets, sp, pp) = routed_rows(T, E, k, seed, routing)
+    n = T * k
+    d_off = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+    d_sp = torch.from_numpy(sp.astype(np.int32)).to(DEV)
+    outs = {}
+    for mode in (moe.MOE_MODE_MFMA, moe.MOE_MODE_GEMV):
+        out = torch.empty((n, H), dtype=torch.float32, device=DEV)
+        nws = moe.moe_grouped_ffn_workspace_size(E, H, I, n, mode)
+        ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+        moe.moe_grouped_w4a16_ffn(layer["experts"], E, H, I, x, d_sp, k, d_off, n, out, mode, ws, nws)
+        outs[mode] = out
+    out_s = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    d_off_s = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    nws = moe.moe_grouped_ffn_workspace_size(1, H, I, T, moe.MOE_MODE_MFMA)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    moe.moe_grouped_w4a16_ffn(layer["shared"], 1, H, I, x, None, 1, d_off_s, T, out_s, moe.MOE_MODE_MFMA, ws, nws)
+    sync()
+    # sampled rows: the first and last rows of the three largest experts, and a spread of others
+    big = np.argsort(-counts, kind="stable")[:3]
+    rows = set()
+    for e in big:
+        rows |= {int(offsets[e]), int(offsets[e + 1]) - 1, int((offsets[e] + offsets[e + 1]) // 2)}
+    rows |= set(np.linspace(0, n - 1, 24).astype(int).tolist())
+    rows = np.array(sorted(rows))
+    experts = set(int(np.searchsorted(offsets, r, side="right") - 1) for r in rows)
+    host = synth.layer_to_numpy(layer, experts=experts)
+    xb = bits_of(x)
+    ref = np.zeros((len(rows), H))
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(offsets, r, side="right") - 1)
+        ref[i] = oracle.expert_ffn(host["experts"], e, oracle.bf16_bits_to_f64(xb[[sp[r] // k]]))[0]
+    got = outs[moe.MOE_MODE_MFMA].cpu().numpy()[rows]
+    assert normwise_err(got, ref) <= TOL_EXPERT
+    # MFMA and GEMV agree everywhere: each is within TOL_EXPERT of the exact
+    # result (their h roundings flip independently), so within twice that
+    assert normwise_err(outs[moe.MOE_MODE_MFMA].cpu().numpy(), outs[moe.MOE_MODE_GEMV].cpu().numpy()) <= 2 * TOL_EXPERT
+    srows = np.unique(np.linspace(0, T - 1, 12).astype(int))
+    ref_s = oracle.expert_ffn(host["shared"], 0, oracle.bf16_bits_to_f64(xb[srows]))
+    assert normwise_err(out_s.cpu().numpy()[srows], ref_s) <= TOL_EXPERT
+
+
+def test_prefill_4096_zipf_sampled():
+    """Flint-shaped prefill: 4096 tokens, Zipf(1.1) routing, NVFP4, composed
+    route -> top-k on skewed logits -> permute -> MFMA grouped FFN (routed and
+    shared) -> combine; sampled tokens against the oracle."""
+    print("prefill 4096", flush=True)
+    H, I, E, k, T = 2048, 768, 256, 6, 4096
+    layer = synth.make_layer(1, H, I, E, k, 5, DEV)
+    x = synth.make_tokens(T, H, 5, DEV)
+    lg = synth.zipf_logits(T, E, 1.1, 5, DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    moe.moe_topk_softmax(lg, T, E, k, ids, w)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    pp = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    nws = moe.moe_permute_workspace_size(T, k, E)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    moe.moe_permute(ids, T, k, E, counts, offsets, sp, pp, None, None, 0, ws, nws)
+    out = torch.empty((T * k, H), dtype=torch.float32, device=DEV)
+    nws = moe.moe_grouped_ffn_workspace_size(E, H, I, T * k)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    moe.moe_grouped_w4a16_ffn(layer["experts"], E, H, I, x, sp, k, offsets, T * k, out, moe.MOE_MODE_AUTO, ws, nws)
+    out_s = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    off_s = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    nws = moe.moe_grouped_ffn_workspace_size(1, H, I, T)
+    ws2 = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    moe.moe_grouped_w4a16_ffn(layer["shared"], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, ws2, nws)
+    y = torch.empty_like(x)
+    moe.moe_combine(out, pp, w, out_s, x, T, k, H, y)
+    sync()
+    # routing of the skewed logits: bit-exact ids for every token
+    lg_np = lg.cpu().numpy()
+    ref_ids = oracle.topk_select(lg_np.astype(np.float64), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    c = counts.cpu().numpy()
+    assert c.max() > 1000 and c.min() >= 1          # the skew the workload asks for
+    tokens = np.unique(np.concatenate([np.linspace(0, T - 1, 10).astype(int), [1, 2, T - 2]]))
+    host = synth.layer_to_numpy(layer, experts=set(ref_ids[tokens].ravel().tolist()))
+    ref = oracle.moe_layer(host, bits_of(x), residual_bits=bits_of(x), logits=lg_np, tokens=tokens)
+    err = normwise_err(oracle.bf16_bits_to_f64(bits_of(y)[tokens]), ref["y"])
+    print("  prefill sampled normwise err %.3e" % err, flush=True)
+    assert err <= TOL_LAYER
+
+
+def test_layer_decode_large_batch_uses_grouped_gemm():
+    print("layer T=200 composed", flush=True)
+    layer = synth.make_layer(2, 2048, 768, 256, 6, 110, DEV)
+    x = synth.make_tokens(200, 2048, 110, DEV)
+    y, ids, w = run_layer(layer, x, x, 200)
+    check_layer(layer, x, x, y, ids, w, tokens=[0, 57, 123, 199])

@@ -273,7 +273,13 @@ def bench_prefill(args, fmt):
 
 
 def bench_chain(args, fmt):
-    """One decode step through 47 chained MoE layers at batch 8, residual add between layers."""
+    """One decode step through 47 chained MoE layers at batch 8.
+
+    Layer l adds its MoE output to the residual stream r: r_{l+1} = r_l + MoE_l(x_l).
+    In the model x_l is the normalised residual; the normalisation is outside the
+    MoE layer, so each layer reads a seeded unit-scale stand-in x_l and the chain
+    runs through the residual (without it, SwiGLU's roughly quadratic growth would
+    overflow bf16 within a few layers)."""
     import torch
     import bit_weight_only_moe_amd as moe
     import synth
@@ -282,7 +288,8 @@ def bench_chain(args, fmt):
     K, W = max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
     layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(4, l), dev) for l in range(NL)]
     Ls = [moe.Layer(l) for l in layers]
-    xs = [synth.make_tokens(T, H, 4, dev)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    xin = [synth.make_tokens(T, H, synth.seed_of(5, l), dev) for l in range(NL)]
+    rs = [synth.make_tokens(T, H, 4, dev)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
     ids = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NL)]
     ws_ = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NL)]
     nws = moe.moe_layer_decode_workspace_size(Ls[0], T)
@@ -290,7 +297,7 @@ def bench_chain(args, fmt):
 
     def step(i, s):
         for l in range(NL):
-            moe.moe_layer_decode(Ls[l], xs[l], xs[l], T, xs[l + 1], ids[l], ws_[l], wsb, nws, stream=s)
+            moe.moe_layer_decode(Ls[l], xin[l], rs[l], T, rs[l + 1], ids[l], ws_[l], wsb, nws, stream=s)
 
     stream = torch.cuda.Stream()
     ms = timed_graph(torch, stream, step, K, W)

@@ -109,6 +109,7 @@ struct DecodeWs {
   uint16_t* h_shared;
   float* o_routed;
   float* o_shared;
+  int32_t* rec;
   void* perm_ws;
   void* mfma_ws;
 };
@@ -131,6 +132,7 @@ size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
   t.h_shared = c.take<uint16_t>((size_t)T * Is);
   t.o_routed = c.take<float>(n * L->H);
   t.o_shared = c.take<float>((size_t)T * L->H);
+  t.rec = c.take<int32_t>(T <= kDecodeMaxT ? moe::layer_decode_rec_ints(T, L->E, L->k) : 0);
   t.perm_ws = c.take<char>(moe::permute_ws_bytes(T, L->k, L->E));
   t.mfma_ws = c.take<char>(T > kDecodeMaxT ? std::max(moe::mfma_ws_bytes(L->E, L->H, L->I, (int)n),
                                                       moe::mfma_ws_bytes(1, L->H, Is, T))
@@ -334,11 +336,21 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
   hipStream_t s = as_stream(stream);
   const int E = L->E, k = L->k, H = L->H;
   const int Is = L->shared ? L->shared->gate.rows : 0;
-  if (moe::layer_decode_lds(T, H, L->I, Is, E, k) > 0)
-    return hip_status(moe::launch_layer_decode(L, x, residual, T, y, d.sync, d.logits, d.ids, d.w, d.offsets,
-                                               d.sorted_pairs, d.pair_pos, d.active, d.h_routed, d.h_shared,
-                                               d.o_routed, d.o_shared, ids_out, w_out, s),
-                      "moe_layer_decode");
+  if (moe::layer_decode_lds(T, H, L->I, Is, E, k) > 0) {
+    moe::LayerDecodeBufs b;
+    b.sync = d.sync;
+    b.logits = d.logits;
+    b.ids = d.ids;
+    b.w = d.w;
+    b.pair_pos = d.pair_pos;
+    b.n_active = d.active;
+    b.rec = d.rec;
+    b.h_routed = d.h_routed;
+    b.h_shared = d.h_shared;
+    b.o_routed = d.o_routed;
+    b.o_shared = d.o_shared;
+    return hip_status(moe::launch_layer_decode(L, x, residual, T, y, b, ids_out, w_out, s), "moe_layer_decode");
+  }
   // Larger batches: composed from the separate kernels (route, group, routed experts, the shared expert as
   // one unit, combine).
   hipError_t e = moe::launch_router_logits(x, L->w_router, T, H, E, d.logits, s);

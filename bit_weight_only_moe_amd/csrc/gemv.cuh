@@ -9,7 +9,10 @@
 // ... so each load instruction of a lane group reads LPR*16 consecutive
 // bytes.  64/LPR rows are in flight per wave.
 //
-// Token staging in LDS, per token, K values:
+// Token staging in LDS, per token, K values, stored piece-transposed: the
+// c-th 16-byte chunk (c = 0..3) of piece p sits at chunk index c*(K/32) + p,
+// so the 64 lanes of a wave, which work on consecutive pieces, read
+// consecutive 16-byte chunks (no LDS bank conflicts).  Within a chunk:
 //   NVFP4: bf16 in natural order (the FP4 convert yields element pairs 2i, 2i+1);
 //   INT4:  bf16 permuted inside every 8-element chunk as x0 x4 x1 x5 x2 x6 x3 x7
 //          (the magic-number unpack yields nibble pairs (s, s+4)), plus the fp32
@@ -21,45 +24,69 @@
 
 namespace moe {
 
-template <bool COH>
-MOE_DEV uint4 load16(const uint4* p) {
-  if (!COH) return *p;
-  const uint64_t a = ld_dev((const uint64_t*)p), b = ld_dev((const uint64_t*)p + 1);
-  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+// Stage rows row_of(0) .. row_of(nt - 1) of `src` (K bf16 values each) into
+// LDS in the FMT layout, piece-transposed: row t at dst + t*K, its INT4
+// piece sums at dsum + t*(K/32).  Each thread takes whole 32-element pieces and issues the
+// loads of two pieces before it writes either, so up to 512 pieces cost one
+// memory round trip.
+// 32 bf16 values (one piece of a token row) in four 16-byte registers.
+struct Piece64 {
+  uint4 a, b, c, d;
+};
+
+// Store one piece (chunks at a stride of `np` 16-byte chunks) in the FMT layout.
+template <int FMT>
+MOE_DEV void store_piece(uint4* __restrict__ dst, int np, float* __restrict__ dsum, const Piece64& v) {
+  if (FMT == kFmtNvfp4) {
+    dst[0] = v.a;
+    dst[np] = v.b;
+    dst[2 * np] = v.c;
+    dst[3 * np] = v.d;
+  } else {
+    float sum = 0.f;
+    const uint4 w4[4] = {v.a, v.b, v.c, v.d};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = w4[c];
+      // elements 0..7 as 16-bit halves of w.x .. w.w
+      const uint32_t e0 = w.x & 0xffffu, e1 = w.x >> 16, e2 = w.y & 0xffffu, e3 = w.y >> 16;
+      const uint32_t e4 = w.z & 0xffffu, e5 = w.z >> 16, e6 = w.w & 0xffffu, e7 = w.w >> 16;
+      uint4 o;
+      o.x = e0 | (e4 << 16);
+      o.y = e1 | (e5 << 16);
+      o.z = e2 | (e6 << 16);
+      o.w = e3 | (e7 << 16);
+      dst[c * np] = o;
+      sum += ((bf16_to_f32(e0) + bf16_to_f32(e1)) + (bf16_to_f32(e2) + bf16_to_f32(e3))) +
+             ((bf16_to_f32(e4) + bf16_to_f32(e5)) + (bf16_to_f32(e6) + bf16_to_f32(e7)));
+    }
+    *dsum = sum;
+  }
 }
 
-// Stage one token row (K bf16 values from global) into LDS in the FMT layout.
-// Thread `tid` of `nthr` handles whole 32-element pieces.  COH: the row was
-// written by another block of the same launch (device-coherent loads).
-template <int FMT, bool COH = false>
-MOE_DEV void stage_token(uint16_t* __restrict__ dst, float* __restrict__ dsum, const uint16_t* __restrict__ src,
-                         int K, int tid, int nthr) {
-  const int npieces = K / 32;
-  for (int p = tid; p < npieces; p += nthr) {
-    const uint4* s = (const uint4*)(src + 32 * p);
-    uint4* d = (uint4*)(dst + 32 * p);
-    if (FMT == kFmtNvfp4) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) d[c] = load16<COH>(s + c);
-    } else {
-      float sum = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 v = load16<COH>(s + c);
-        // elements 0..7 as 16-bit halves of v.x .. v.w
-        const uint32_t e0 = v.x & 0xffffu, e1 = v.x >> 16, e2 = v.y & 0xffffu, e3 = v.y >> 16;
-        const uint32_t e4 = v.z & 0xffffu, e5 = v.z >> 16, e6 = v.w & 0xffffu, e7 = v.w >> 16;
-        uint4 o;
-        o.x = e0 | (e4 << 16);
-        o.y = e1 | (e5 << 16);
-        o.z = e2 | (e6 << 16);
-        o.w = e3 | (e7 << 16);
-        d[c] = o;
-        sum += ((bf16_to_f32(e0) + bf16_to_f32(e1)) + (bf16_to_f32(e2) + bf16_to_f32(e3))) +
-               ((bf16_to_f32(e4) + bf16_to_f32(e5)) + (bf16_to_f32(e6) + bf16_to_f32(e7)));
-      }
-      dsum[p] = sum;
-    }
+MOE_DEV Piece64 load_piece64(const uint16_t* __restrict__ src) {
+  const uint4* s = (const uint4*)src;
+  return Piece64{s[0], s[1], s[2], s[3]};
+}
+
+// Stage rows row_of(0) .. row_of(nt - 1) of `src` (K bf16 values each) into
+// LDS in the FMT layout, piece-transposed: row t at dst + t*K, its INT4
+// piece sums at dsum + t*(K/32).  Each thread takes whole 32-element pieces and issues the
+// loads of two pieces before it writes either, so up to 512 pieces cost one
+// memory round trip.
+template <int FMT, typename RowOf>
+MOE_DEV void stage_rows(uint16_t* __restrict__ dst, float* __restrict__ dsum, const uint16_t* __restrict__ src,
+                        RowOf row_of, int nt, int K) {
+  const int ppt = K / 32, total = nt * ppt, nthr = blockDim.x;
+  for (int p0 = threadIdx.x; p0 < total; p0 += 2 * nthr) {
+    const int p1 = p0 + nthr;
+    const int t0 = p0 / ppt, t1 = p1 / ppt;
+    const int c0 = p0 - t0 * ppt, c1 = p1 - t1 * ppt;
+    const Piece64 v0 = load_piece64(src + (size_t)row_of(t0) * K + 32 * c0);
+    Piece64 v1;
+    if (p1 < total) v1 = load_piece64(src + (size_t)row_of(t1) * K + 32 * c1);
+    store_piece<FMT>((uint4*)(dst + (size_t)t0 * K) + c0, ppt, dsum + p0, v0);
+    if (p1 < total) store_piece<FMT>((uint4*)(dst + (size_t)t1 * K) + c1, ppt, dsum + p1, v1);
   }
 }
 
@@ -90,8 +117,8 @@ MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t
 
 // Accumulate the dot products of piece p (already loaded) with nt <= NT
 // staged tokens into acc[t] (without the NVFP4 tensor scale).
-//   xs   : LDS tokens, token t at xs + t*xstride (bf16 elements)
-//   xsum : LDS piece sums (INT4), token t at xsum + t*sstride
+//   xs   : LDS tokens, token t at xs + t*xstride (bf16 elements), piece-transposed
+//   xsum : LDS piece sums (INT4), token t at xsum + t*sstride; sstride = xstride / 32
 template <int FMT, int NT>
 MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs, int xstride,
                        const float* __restrict__ xsum, int sstride, int nt, float (&acc)[NT]) {
@@ -125,8 +152,8 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t < nt) {
-      const uint4* xp = (const uint4*)(xs + t * xstride + 32 * p);
-      const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+      const uint4* xp = (const uint4*)(xs + t * xstride) + p;
+      const uint4 x0 = xp[0], x1 = xp[sstride], x2 = xp[2 * sstride], x3 = xp[3 * sstride];
       float d0 = 0.f, d1 = 0.f;
       d0 = dot2_bf16(q[0], x0.x, d0); d0 = dot2_bf16(q[1], x0.y, d0);
       d0 = dot2_bf16(q[2], x0.z, d0); d0 = dot2_bf16(q[3], x0.w, d0);

@@ -59,54 +59,32 @@ hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* cod
 
 // ---------------------------------------------------------------- router GEMV
 // logits[t, e] = sum_h x[t, h] * w_router[e, h], fp32 accumulation.
-// Block: 4 waves = 4 experts; up to kRouteTok tokens staged in LDS as bf16.
-constexpr int kRouteTok = 8;
+// Block: 4 waves = 4 experts; up to kRouteTok tokens staged in LDS as bf16
+// (at most 64 KB).
+constexpr int kRouteTok = 16;
 
 __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                        int T, int H, int E, int tpb, float* __restrict__ logits) {
-  extern __shared__ uint16_t xs[];  // [tpb][H], tpb <= kRouteTok
+  extern __shared__ __align__(16) uint16_t xs[];  // [tpb][H], tpb <= kRouteTok
   const int t0 = blockIdx.y * tpb;
   const int nt = min(tpb, T - t0);
-  // stage tokens: 8 bytes per thread-step
-  for (int i = threadIdx.x; i < nt * H / 4; i += blockDim.x) {
-    const int t = i / (H / 4), c = i % (H / 4);
-    ((uint2*)xs)[t * (H / 4) + c] = ((const uint2*)(x + (size_t)(t0 + t) * H))[c];
-  }
-  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
+  float4 wv[kRouterC];
+  if (e < E) router_prefetch(wr + (size_t)e * H, H, lane, wv);
+  copy_to_lds((uint4*)xs, (const uint4*)(x + (size_t)t0 * H), nt * H / 8);
+  __syncthreads();
   if (e >= E) return;
   float acc[kRouteTok];
+  router_dots<kRouteTok>(wr + (size_t)e * H, xs, H, nt, lane, acc, wv);
 #pragma unroll
-  for (int t = 0; t < kRouteTok; ++t) acc[t] = 0.f;
-  const float4* wrow = (const float4*)(wr + (size_t)e * H);
-  for (int c = lane; c < H / 4; c += 64) {
-    const float4 w = wrow[c];
-#pragma unroll
-    for (int t = 0; t < kRouteTok; ++t) {
-      if (t < nt) {
-        const uint2 xv = ((const uint2*)xs)[t * (H / 4) + c];
-        float a = acc[t];
-        a = fmaf(w.x, bf16_to_f32(xv.x & 0xffffu), a);
-        a = fmaf(w.y, bf16_to_f32(xv.x >> 16), a);
-        a = fmaf(w.z, bf16_to_f32(xv.y & 0xffffu), a);
-        a = fmaf(w.w, bf16_to_f32(xv.y >> 16), a);
-        acc[t] = a;
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < kRouteTok; ++t) {
-    if (t < nt) {
-      const float v = group_sum_last<64>(acc[t]);  // same reduction order as the fused decode router
-      if (lane == 63) logits[(size_t)(t0 + t) * E + e] = v;
-    }
-  }
+  for (int t = 0; t < kRouteTok; ++t)
+    if (t < nt && lane == 63) logits[(size_t)(t0 + t) * E + e] = acc[t];
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                                 hipStream_t s) {
-  const int tpb = std::max(1, std::min(kRouteTok, 16384 / H));  // <= 32 KB of LDS
+  const int tpb = std::max(1, std::min(kRouteTok, 32768 / H));  // <= 64 KB of LDS
   dim3 grid((E + 3) / 4, (T + tpb - 1) / tpb);
   const size_t lds = (size_t)tpb * H * sizeof(uint16_t);
   hipLaunchKernelGGL(k_router_logits, grid, dim3(256), lds, s, x, wr, T, H, E, tpb, logits);

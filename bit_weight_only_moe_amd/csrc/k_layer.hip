@@ -10,17 +10,21 @@
 // stores and take a ticket from an atomic counter, and the block that takes
 // the final ticket continues with a device-scope acquire.
 //
-//   launch 1  router blocks: logits of 4 experts (one per wave); the last
-//             router block does top-k, softmax and the expert grouping.
-//             shared-expert blocks (same grid): gate/up + SwiGLU, which needs
-//             no routing, so its weights stream while the router runs.
-//   launch 2  routed gate/up + SwiGLU: one (touched expert, 16-row slice) per
+//   launch 1  router blocks: logits of 4 experts (one per wave) for a batch
+//             of up to 4 tokens.  The last router block of a batch does the
+//             batch's top-k + softmax (one token per wave); the last batch to
+//             finish groups every (token, choice) pair by expert and writes
+//             one record per touched expert.  Shared-expert blocks (same
+//             grid): gate/up + SwiGLU, which needs no routing, so its weights
+//             stream while the router runs.
+//   launch 2  routed gate/up + SwiGLU: one (record, row slice of I) per
 //             block; each touched expert's weights are read once for all the
 //             tokens that chose it.
-//   launch 3  down projection: one (unit = touched or shared expert, 64-row
-//             slice of H) per block, fp32 outputs to the workspace; the last
-//             block of each slice combines y = residual + sum_j w_j o_j +
-//             o_shared in that fixed order and rounds to bf16.
+//   launch 3  down projection: one (unit = record or shared-expert token
+//             batch, row slice of H) per block, fp32 outputs to the
+//             workspace; the last block of each slice combines
+//             y = residual + sum_j w_j o_j + o_shared in that fixed order and
+//             rounds to bf16.
 //
 // Every block loads all of its weight pieces before it uses any, so one
 // memory round trip covers a block's whole share of the expert bytes.
@@ -32,11 +36,11 @@ namespace moe {
 
 #ifdef MOE_TRACE
 // Per-block phase timestamps (100 MHz constant clock) for development builds.
-__device__ unsigned long long g_trace[3][65536 * 4];
+__device__ unsigned long long g_trace[3][65536 * 8];
 #define MOE_TRACE_AT(kern, slot)                                                      \
   do {                                                                                \
     if (threadIdx.x == 0 && blockIdx.x < 65536)                                       \
-      g_trace[kern][blockIdx.x * 4 + (slot)] = __builtin_amdgcn_s_memrealtime();      \
+      g_trace[kern][blockIdx.x * 8 + (slot)] = __builtin_amdgcn_s_memrealtime();      \
   } while (0)
 #else
 #define MOE_TRACE_AT(kern, slot) \
@@ -44,13 +48,19 @@ __device__ unsigned long long g_trace[3][65536 * 4];
   } while (0)
 #endif
 
-constexpr int kRG = 16;      // gate/up rows per block
-constexpr int kRD = 64;      // down rows per block
-constexpr int kMaxPc = 8;    // weight pieces per lane held in registers per matrix
+constexpr int kRG = 16;      // gate/up rows per block (4 when T == 1)
+constexpr int kRD = 64;      // down rows per block (32 when T == 1)
+constexpr int kRDMin = 32;   // smallest down slice: bounds the number of slice tickets
+constexpr int kMaxPcG = 4;   // gate/up weight pieces per lane held in registers, per matrix
+constexpr int kMaxPcD = 8;   // down weight pieces per lane held in registers
+constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
+constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
+constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
 
 // Synchronisation words (ints) at the start of the workspace, 64 bytes apart.
-constexpr int kTicketRouter = 0;
-constexpr int kTicketSlice = 16;  // + 16 * slice
+constexpr int kTicketGroup = 0;                         // batches routed
+constexpr int kTicketBatch = 16;                        // + 16 * batch: router blocks of a batch done
+constexpr int kTicketSlice = 16 * (1 + kMaxBatches);    // + 16 * slice: down units of a slice done
 
 struct LayerArgs {
   int T, H, I, Is, E, k;
@@ -64,30 +74,36 @@ struct LayerArgs {
   float* logits;             // [T, E]
   int32_t* ids;              // [T*k]
   float* w;                  // [T*k]
-  int32_t* offsets;          // [E + 1]
-  int32_t* sorted_pairs;     // [T*k]
   int32_t* pair_pos;         // [T*k]
-  int32_t* active;           // [1 + E]
+  int32_t* n_active;         // [1]
+  int32_t* rec;              // [max_active, kRec]
   uint16_t* h_routed;        // [T*k, I]
   uint16_t* h_shared;        // [T, Is]
   float* o_routed;           // [T*k, H]
   float* o_shared;           // [T, H]
   int32_t* ids_out;
   float* w_out;
-  int nR, nS;                // launch 1 layout
-  int slices_r;              // launch 2: gate/up slices per routed expert
-  int slices_d;              // launch 3: row slices of H
+  int max_active;            // min(E, T*k)
+  int rt;                    // tokens per router block
+  int nRe, nR;               // router blocks: expert groups of 4, total (expert groups x token batches)
+  int nsb;                   // shared-expert token batches of NT tokens (0: no shared expert)
+  int rg, rd;                // rows per gate/up block, per down block
+  int ss_r;                  // shared gate/up row slices
+  int slices_r;              // routed gate/up row slices per expert
+  int slices_d;              // down row slices of H
   int lpr_h, lpr_i, lpr_is;
+  int down_stage_bytes;      // launch 3: LDS bytes of the token staging (16-byte multiple)
 };
 
+
 // ------------------------------------------------------------------ gate/up
-// Load this lane's pieces c0 .. c0+kMaxPc-1 (row iteration c / ppl, piece
+// Load this lane's pieces c0 .. c0+kMaxPcG-1 (row iteration c / ppl, piece
 // c % ppl) of the gate and up rows into registers.
 template <int FMT>
 MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, int npc, int ppl, int lpr, int lir,
-                               int row0, int row_step, int i1, RawPiece (&rg)[kMaxPc], RawPiece (&ru)[kMaxPc]) {
+                               int row0, int row_step, int i1, RawPiece (&rg)[kMaxPcG], RawPiece (&ru)[kMaxPcG]) {
 #pragma unroll
-  for (int q = 0; q < kMaxPc; ++q) {
+  for (int q = 0; q < kMaxPcG; ++q) {
     const int c = c0 + q;
     const int i = row0 + row_step * (c / ppl);
     if (c < npc && i < i1) {
@@ -114,28 +130,27 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
   const float tsg = tensor_scale<FMT>(G, e), tsu = tensor_scale<FMT>(U, e);
   // When every piece fits in registers they are loaded once, before the
   // tokens are staged, so both memory latencies overlap.
-  const bool resident = npc <= kMaxPc;
-  RawPiece rg[kMaxPc], ru[kMaxPc];
+  const bool resident = npc <= kMaxPcG;
+  RawPiece rg[kMaxPcG], ru[kMaxPcG];
   const int row0 = i0 + wave * rpw + rsub;
   if (resident) load_gateup_chunk<FMT>(G, U, e, 0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
   for (int rb = r0; rb < r1; rb += NT) {
     const int nt = min(NT, r1 - rb);
     __syncthreads();
-    for (int t = 0; t < nt; ++t)
-      stage_token<FMT>(xs + t * H, xsum + t * (H / 32), x + (size_t)tok_of(rb + t) * H, H, tid, 256);
+    stage_rows<FMT>(xs, xsum, x, [&](int t) { return tok_of(rb + t); }, nt, H);
     __syncthreads();
-    MOE_TRACE_AT(kern, 1);
+    MOE_TRACE_AT(kern, 2);
     float ag[NT], au[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
-    for (int c0 = 0; c0 < npc; c0 += kMaxPc) {
+    for (int c0 = 0; c0 < npc; c0 += kMaxPcG) {
       // piece c of this lane: row iteration c / ppl, piece index c % ppl
       if (!resident) load_gateup_chunk<FMT>(G, U, e, c0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
 #pragma unroll
-      for (int q = 0; q < kMaxPc; ++q) {
+      for (int q = 0; q < kMaxPcG; ++q) {
         const int c = c0 + q;
         if (c < npc) {
-          const int i = i0 + wave * rpw + rsub + 4 * rpw * (c / ppl);
+          const int i = row0 + 4 * rpw * (c / ppl);
           if (i < i1) {
             const int p = lir + (c % ppl) * lpr;
             piece_dot<FMT, NT>(rg[q], p, xs, H, xsum, H / 32, nt, ag);
@@ -162,7 +177,7 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
       }
     }
   }
-  MOE_TRACE_AT(kern, 2);
+  MOE_TRACE_AT(kern, 3);
 }
 
 // ------------------------------------------------------------------ down
@@ -181,12 +196,13 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   uint16_t* xs = (uint16_t*)smem;
   float* xsum = (float*)(smem + (size_t)NT * K * sizeof(uint16_t));
   const float ts = tensor_scale<FMT>(D, e);
-  const bool resident = npc <= kMaxPc;  // every piece stays in registers across token batches
-  RawPiece rd[kMaxPc];
+  const bool resident = npc <= kMaxPcD;  // every piece stays in registers across token batches
+  const int row0 = n0 + wave * rpw + rsub;
+  RawPiece rd[kMaxPcD];
   if (resident) {
 #pragma unroll
-    for (int q = 0; q < kMaxPc; ++q) {
-      const int n = n0 + wave * rpw + rsub + 4 * rpw * (q / ppl);
+    for (int q = 0; q < kMaxPcD; ++q) {
+      const int n = row0 + 4 * rpw * (q / ppl);
       if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
                                                       lir + (q % ppl) * lpr);
     }
@@ -194,28 +210,28 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   for (int rb = r0; rb < r1; rb += NT) {
     const int nt = min(NT, r1 - rb);
     __syncthreads();
-    for (int t = 0; t < nt; ++t) stage_token<FMT>(xs + t * K, xsum + t * (K / 32), hin + (size_t)(rb + t) * K, K, tid, 256);
+    stage_rows<FMT>(xs, xsum, hin, [rb](int t) { return rb + t; }, nt, K);
     __syncthreads();
-    MOE_TRACE_AT(2, 1);
+    MOE_TRACE_AT(2, 2);
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-    for (int c0 = 0; c0 < npc; c0 += kMaxPc) {
+    for (int c0 = 0; c0 < npc; c0 += kMaxPcD) {
       if (!resident) {
 #pragma unroll
-        for (int q = 0; q < kMaxPc; ++q) {
+        for (int q = 0; q < kMaxPcD; ++q) {
           const int c = c0 + q;
-          const int n = n0 + wave * rpw + rsub + 4 * rpw * (c / ppl);
+          const int n = row0 + 4 * rpw * (c / ppl);
           if (c < npc && n < n1)
             rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
                                     lir + (c % ppl) * lpr);
         }
       }
 #pragma unroll
-      for (int q = 0; q < kMaxPc; ++q) {
+      for (int q = 0; q < kMaxPcD; ++q) {
         const int c = c0 + q;
         if (c < npc) {
-          const int n = n0 + wave * rpw + rsub + 4 * rpw * (c / ppl);
+          const int n = row0 + 4 * rpw * (c / ppl);
           if (n < n1) piece_dot<FMT, NT>(rd[q], lir + (c % ppl) * lpr, xs, K, xsum, K / 32, nt, acc);
           if (c % ppl == ppl - 1) {  // the row's last piece
 #pragma unroll
@@ -241,6 +257,10 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
 }
 
 // ------------------------------------------------------------------ launch 1
+// Blocks [0, nR): router, 4 experts (one per wave) x up to rt tokens.  The
+// block that takes the last router ticket does top-k + softmax for every
+// token and groups the (token, choice) pairs by expert.
+// Blocks [nR, ...): shared expert gate/up, one (row slice, token batch) each.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -249,88 +269,97 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, E = a.E;
   if ((int)blockIdx.x >= a.nR) {
-    const int slice = blockIdx.x - a.nR;
-    const int i0 = slice * kRG, i1 = min(a.Is, i0 + kRG);
-    gateup_rows<FMT, NT>(a.sgate, a.sup, 0, 0, T, i0, i1, H, a.x, [](int r) { return r; }, a.h_shared, a.Is,
-                         a.lpr_h, smem, 0);
-    MOE_TRACE_AT(0, 3);
+    const int b = blockIdx.x - a.nR;
+    const int slice = b % a.ss_r, r0 = (b / a.ss_r) * NT;
+    const int i0 = slice * a.rg, i1 = min(a.Is, i0 + a.rg);
+    gateup_rows<FMT, NT>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x, [](int r) { return r; },
+                         a.h_shared, a.Is, a.lpr_h, smem, 0);
+    MOE_TRACE_AT(0, 4);
     return;
   }
-  // router: one expert per wave, all tokens; tokens staged in LDS 8 at a time,
-  // the router row streamed in chunks of 4 float4 per lane
-  const int e = blockIdx.x * 4 + wave;
-  constexpr int kC = 4;
-  constexpr int kTB = 8;
-  const int nc = H / 4;
-  uint2* xs = (uint2*)smem;  // [kTB][H / 4]
-  for (int t0 = 0; t0 < T; t0 += kTB) {
-    const int nt = min(kTB, T - t0);
+  const int nb = a.nR / a.nRe;  // token batches
+  const int batch = blockIdx.x / a.nRe;
+  const int t0 = batch * a.rt, nt = min(a.rt, T - t0);
+  {
+    const int e = (blockIdx.x % a.nRe) * 4 + wave;
+    float4 wv[kRouterC];
+    if (e < E) router_prefetch(a.w_router + (size_t)e * H, H, lane, wv);
+    copy_to_lds((uint4*)smem, (const uint4*)(a.x + (size_t)t0 * H), nt * H / 8);
     __syncthreads();
-    for (int i = tid; i < nt * nc; i += 256) xs[i] = ((const uint2*)(a.x + (size_t)t0 * H))[i];
-    __syncthreads();
+    MOE_TRACE_AT(0, 1);
     if (e < E) {
-      const float4* wr = (const float4*)(a.w_router + (size_t)e * H);
-      float s[kTB];
+      float acc[kRouteT];
+      router_dots<kRouteT>(a.w_router + (size_t)e * H, (const uint16_t*)smem, H, nt, lane, acc, wv);
+      // device-coherent stores: the block that takes the batch's last ticket reads them
 #pragma unroll
-      for (int tt = 0; tt < kTB; ++tt) s[tt] = 0.f;
-      for (int cb = 0; cb < nc; cb += 64 * kC) {
-        float4 wv[kC];
-#pragma unroll
-        for (int q = 0; q < kC; ++q)
-          if (cb + lane + 64 * q < nc) wv[q] = wr[cb + lane + 64 * q];
-#pragma unroll
-        for (int tt = 0; tt < kTB; ++tt) {
-          if (tt < nt) {
-#pragma unroll
-            for (int q = 0; q < kC; ++q) {
-              const int c = cb + lane + 64 * q;
-              if (c < nc) {
-                const uint2 xv = xs[tt * nc + c];
-                s[tt] = fmaf(wv[q].x, bf16_to_f32(xv.x & 0xffffu), s[tt]);
-                s[tt] = fmaf(wv[q].y, bf16_to_f32(xv.x >> 16), s[tt]);
-                s[tt] = fmaf(wv[q].z, bf16_to_f32(xv.y & 0xffffu), s[tt]);
-                s[tt] = fmaf(wv[q].w, bf16_to_f32(xv.y >> 16), s[tt]);
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < kTB; ++tt) {
-        if (tt < nt) {
-          const float v = group_sum_last<64>(s[tt]);
-          if (lane == 63) a.logits[(size_t)(t0 + tt) * E + e] = v;
-        }
-      }
+      for (int t = 0; t < kRouteT; ++t)
+        if (t < nt && lane == 63) st_dev(a.logits + (size_t)(t0 + t) * E + e, acc[t]);
     }
   }
-  MOE_TRACE_AT(0, 1);
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    ticket = __hip_atomic_fetch_add(a.sync + kTicketRouter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
   MOE_TRACE_AT(0, 2);
-  if (ticket != a.nR - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this block's stores are complete
+  __syncthreads();
+  int* ctr = a.sync + kTicketBatch + 16 * batch;
+  if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  MOE_TRACE_AT(0, 3);
+  if (ticket != a.nRe - 1) return;
 
-  // Last router block: all logits are stored.  Top-k + softmax per token,
-  // then the stable grouping of pairs p = t*k + j by expert.  ids within a
-  // token are distinct, so the rank of (t, j) among its expert's pairs is the
-  // number of earlier tokens that chose the same expert (a 64-bit mask per
-  // expert, T <= 64).
+  // Last router block of this token batch: every logit of its nt <= 4 tokens
+  // is stored.  Top-k + softmax, one token per wave.
   if (tid == 0) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    a.sync[kTicketRouter] = 0;  // ready for the next call
+    *ctr = 0;  // ready for the next call
   }
   __syncthreads();
+  MOE_TRACE_AT(0, 5);
   const int k = a.k, n = T * k;
-  unsigned long long* mask = (unsigned long long*)smem;  // [E]
-  int32_t* s_ids = (int32_t*)(mask + E);                  // [n]
-  float* s_w = (float*)(s_ids + n);                       // [n]
-  int32_t* off = (int32_t*)(s_w + n);                     // [E + 1]
-  int* scan_tmp = (int*)(off + E + 1);                    // [17]
-  for (int t = wave; t < T; t += 4) wave_topk_softmax(a.logits + (size_t)t * E, E, k, lane, s_ids + t * k, s_w + t * k);
+  int32_t* s_ids = (int32_t*)smem;                                      // [n]
+  float* s_w = (float*)(s_ids + n);                                     // [n]
+  float* s_log = s_w + n;                                               // [kRouteT, E]
+  unsigned long long* mask = (unsigned long long*)(((uintptr_t)(s_log + kRouteT * E) + 7) & ~(uintptr_t)7);  // [E]
+  int32_t* off = (int32_t*)(mask + E);                                  // [E + 1]
+  int* scan_tmp = (int*)(off + E + 1);                                  // [17]
+  copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
+  __syncthreads();
+  if (wave < nt) wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
+  __syncthreads();
+  MOE_TRACE_AT(0, 6);
+  const int p0 = t0 * k, p1 = (t0 + nt) * k;  // this batch's pairs
+  if (nb > 1) {
+    // Publish this batch's choices; the last batch to finish groups all tokens.
+    for (int p = p0 + tid; p < p1; p += 256) {
+      st_dev(a.ids + p, s_ids[p]);
+      st_dev(a.w + p, s_w[p]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(a.sync + kTicketGroup, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != nb - 1) return;
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      a.sync[kTicketGroup] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < n; p += 256) {
+      if (p < p0 || p >= p1) {
+        s_ids[p] = a.ids[p];
+        s_w[p] = a.w[p];
+      }
+    }
+    __syncthreads();
+    MOE_TRACE_AT(0, 7);
+  }
+
+  // Every token's choices are in LDS.  Stable grouping of pairs p = t*k + j
+  // by expert: ids within a token are distinct, so the rank of (t, j) among
+  // its expert's pairs is the number of earlier tokens that chose the same
+  // expert (a 64-bit mask per expert, T <= 64).  Each touched expert, in
+  // ascending id order, gets a record: expert, first row of its pairs in the
+  // grouped order, row count, and the token of each row; records past the
+  // last touched expert get expert -1.
   for (int i = tid; i < E; i += 256) mask[i] = 0ull;
   __syncthreads();
   for (int p = tid; p < n; p += 256) atomicOr(&mask[s_ids[p]], 1ull << (p / k));
@@ -351,75 +380,101 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     const int ee = tid * 4 + q;
     if (ee < E) {
       off[ee] = pre;
-      a.offsets[ee] = pre;
-      if (cnt[q] > 0) a.active[1 + apre++] = ee;
+      if (cnt[q] > 0) {
+        int32_t* r = a.rec + (size_t)(apre++) * kRec;
+        r[0] = ee;
+        r[1] = pre;
+        r[2] = cnt[q];
+        r[3] = 0;
+        unsigned long long m = mask[ee];
+        for (int i = 0; m; ++i, m &= m - 1ull) r[4 + i] = __builtin_ctzll(m);
+      }
       pre += cnt[q];
     }
   }
-  if (tid == 0) {
-    off[E] = total;
-    a.offsets[E] = total;
-    a.active[0] = ntot;
-  }
+  for (int u = ntot + tid; u < a.max_active; u += 256) a.rec[(size_t)u * kRec] = -1;
+  if (tid == 0) a.n_active[0] = ntot;
   __syncthreads();
   for (int p = tid; p < n; p += 256) {
     const int t = p / k, ee = s_ids[p];
-    const int pos = off[ee] + __popcll(mask[ee] & ((1ull << t) - 1ull));
-    a.sorted_pairs[pos] = p;
-    a.pair_pos[p] = pos;
-    a.ids[p] = ee;
-    a.w[p] = s_w[p];
+    a.pair_pos[p] = off[ee] + __popcll(mask[ee] & ((1ull << t) - 1ull));
+    if (nb == 1) {
+      a.ids[p] = ee;
+      a.w[p] = s_w[p];
+    }
     if (a.ids_out) {
       a.ids_out[p] = ee;
       a.w_out[p] = s_w[p];
     }
   }
-  MOE_TRACE_AT(0, 3);
+  MOE_TRACE_AT(0, 4);
 }
 
 // ------------------------------------------------------------------ launch 2
+// One (routed-unit record, 16-row slice of I) per block.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(256) k_layer_gateup(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_rec[kRec];
   MOE_TRACE_AT(1, 0);
   const int unit = blockIdx.x / a.slices_r;
-  if (unit >= a.active[0]) return;
-  const int e = a.active[1 + unit];
-  const int i0 = (blockIdx.x % a.slices_r) * kRG, i1 = min(a.I, i0 + kRG);
-  const int32_t* sp = a.sorted_pairs;
-  const int k = a.k;
-  gateup_rows<FMT, NT>(a.gate, a.up, e, a.offsets[e], a.offsets[e + 1], i0, i1, a.H, a.x,
-                       [sp, k](int r) { return sp[r] / k; }, a.h_routed, a.I, a.lpr_h, smem, 1);
-  MOE_TRACE_AT(1, 3);
+  if (threadIdx.x < kRec) s_rec[threadIdx.x] = a.rec[(size_t)unit * kRec + threadIdx.x];
+  __syncthreads();
+  MOE_TRACE_AT(1, 1);
+  const int e = s_rec[0];
+  if (e < 0) return;
+  const int r0 = s_rec[1];
+  const int i0 = (blockIdx.x % a.slices_r) * a.rg, i1 = min(a.I, i0 + a.rg);
+  gateup_rows<FMT, NT>(a.gate, a.up, e, r0, r0 + s_rec[2], i0, i1, a.H, a.x,
+                       [r0](int r) { return s_rec[4 + r - r0]; }, a.h_routed, a.I, a.lpr_h, smem, 1);
+  MOE_TRACE_AT(1, 4);
 }
 
 // ------------------------------------------------------------------ launch 3
+// One (unit, 64-row slice of H) per block; units are the routed records,
+// then the shared expert's token batches.  fp32 outputs go to the
+// workspace; the last block of each slice combines
+// y = residual + sum_j w_j o_j + o_shared in that fixed order.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int ticket;
+  __shared__ int s_rec[kRec];
+  __shared__ int ticket, s_nact;
   MOE_TRACE_AT(2, 0);
   const int tid = threadIdx.x;
-  const int T = a.T, H = a.H, k = a.k;
+  const int T = a.T, H = a.H, k = a.k, n = T * k;
   const int slice = blockIdx.x % a.slices_d, unit = blockIdx.x / a.slices_d;
-  const int n_active = a.active[0];
-  const bool has_shared = a.sgate.codes != nullptr;
-  const int units = n_active + (has_shared ? 1 : 0);
-  if (unit >= units) return;
-  const int n0 = slice * kRD, n1 = min(H, n0 + kRD);
-  if (unit < n_active) {
-    const int e = a.active[1 + unit];
-    down_rows<FMT, NT>(a.down, e, a.offsets[e], a.offsets[e + 1], n0, n1, a.h_routed, a.o_routed, a.lpr_i, true,
+  const bool routed = unit < a.max_active;
+  // the combine's weights and pair positions (written by launch 1), loaded
+  // with the record so the last block needs one more round trip only
+  float* s_w = (float*)(smem + a.down_stage_bytes);  // [n]
+  int32_t* s_pp = (int32_t*)(s_w + n);                // [n]
+  if (routed && tid < kRec) s_rec[tid] = a.rec[(size_t)unit * kRec + tid];
+  if (tid == 255) s_nact = a.n_active[0];
+  for (int p = tid; p < n; p += 256) {
+    s_w[p] = a.w[p];
+    s_pp[p] = a.pair_pos[p];
+  }
+  __syncthreads();
+  MOE_TRACE_AT(2, 1);
+  const int n0 = slice * a.rd, n1 = min(H, n0 + a.rd);
+  if (routed) {
+    const int e = s_rec[0];
+    if (e < 0) return;
+    down_rows<FMT, NT>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed, a.o_routed, a.lpr_i, true,
                        smem);
   } else {
-    down_rows<FMT, NT>(a.sdown, 0, 0, T, n0, n1, a.h_shared, a.o_shared, a.lpr_is, true, smem);
+    const int r0 = (unit - a.max_active) * NT;
+    down_rows<FMT, NT>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared, a.lpr_is, true, smem);
   }
-  MOE_TRACE_AT(2, 2);
+  MOE_TRACE_AT(2, 3);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
+  const int units = s_nact + a.nsb;
   int* ctr = a.sync + kTicketSlice + 16 * slice;
   if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  MOE_TRACE_AT(2, 4);
   if (ticket != units - 1) return;
   // last block of this slice: every unit's rows [n0, n1) are stored
   if (tid == 0) {
@@ -427,16 +482,24 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     *ctr = 0;
   }
   __syncthreads();
+  const bool has_shared = a.nsb > 0;
   const int rows = n1 - n0;
   for (int idx = tid; idx < T * rows; idx += 256) {
-    const int t = idx / rows, n = n0 + idx % rows;
+    const int t = idx / rows, c = n0 + idx % rows;
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = j < k ? a.o_routed[(size_t)s_pp[t * k + j] * H + c] : 0.f;
+    const float os = has_shared ? a.o_shared[(size_t)t * H + c] : 0.f;
+    const float rs = a.residual ? bf16_to_f32(a.residual[(size_t)t * H + c]) : 0.f;
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(a.w[t * k + j], a.o_routed[(size_t)a.pair_pos[t * k + j] * H + n], acc);
-    if (has_shared) acc += a.o_shared[(size_t)t * H + n];
-    if (a.residual) acc += bf16_to_f32(a.residual[(size_t)t * H + n]);
-    a.y[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(acc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) acc = fmaf(s_w[t * k + j], o[j], acc);
+    if (has_shared) acc += os;
+    if (a.residual) acc += rs;
+    a.y[(size_t)t * H + c] = (uint16_t)f32_to_bf16_rne(acc);
   }
-  MOE_TRACE_AT(2, 3);
+  MOE_TRACE_AT(2, 5);
 }
 
 // ------------------------------------------------------------------ grouped FFN (composed path)
@@ -500,19 +563,40 @@ static MatDev mat_dev(const moe_w4_matrix& m) {
   return d;
 }
 
-static int layer_nt(int T) { return T == 1 ? 1 : (T <= 4 ? 4 : 8); }
+static int layer_nt(int T) { return T == 1 ? 1 : 4; }
 
-size_t layer_decode_lds(int T, int H, int I, int Is, int E, int k) {
-  if (T < 1 || T > 64 || E > 1024 || H > 4096) return 0;
-  const int NT = layer_nt(T), Kmax = std::max(I, Is);
-  const size_t stage_h = (size_t)NT * H * 2 + (size_t)NT * (H / 32) * 4;
-  const size_t stage_i = (size_t)NT * Kmax * 2 + (size_t)NT * (Kmax / 32) * 4;
-  const size_t route = (size_t)E * 8 + (size_t)T * k * 8 + (size_t)(E + 1) * 4 + 17 * 4;
-  const size_t lds = std::max(stage_h, std::max(stage_i, route));
-  return lds <= 64 * 1024 ? lds : 0;
+static size_t stage_bytes(int NT, int K) { return (size_t)NT * K * 2 + (size_t)NT * (K / 32) * 4; }
+
+// Dynamic LDS of the three decode launches; 0 when the shape is outside the
+// decode path (more than 64 tokens, E > 1024, H > 4096, or > 64 KB).
+struct DecodeLds {
+  size_t route, gateup, down;
+};
+
+static int router_tokens(int T) { return std::min(kRouteT, T); }
+
+static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+static DecodeLds decode_lds(int T, int H, int I, int Is, int E, int k) {
+  DecodeLds d{0, 0, 0};
+  if (T < 1 || T > 64 || E > 1024 || H > 4096) return d;
+  const int NT = layer_nt(T);
+  const size_t tables = (size_t)T * k * 8 + (size_t)kRouteT * E * 4 + 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 17 * 4;
+  const size_t route = std::max((size_t)router_tokens(T) * H * 2, std::max(tables, stage_bytes(NT, H)));
+  const size_t gateup = stage_bytes(NT, H);
+  const size_t down = align16(stage_bytes(NT, std::max(I, Is))) + (size_t)T * k * 8;
+  if (std::max(route, std::max(gateup, down)) > 64 * 1024) return d;
+  return DecodeLds{route, gateup, down};
 }
 
-int layer_decode_sync_words(int H) { return kTicketSlice + 16 * ((H + kRD - 1) / kRD); }
+size_t layer_decode_lds(int T, int H, int I, int Is, int E, int k) {
+  const DecodeLds d = decode_lds(T, H, I, Is, E, k);
+  return std::max(d.route, std::max(d.gateup, d.down));
+}
+
+int layer_decode_sync_words(int H) { return kTicketSlice + 16 * ((H + kRDMin - 1) / kRDMin); }
+
+size_t layer_decode_rec_ints(int T, int E, int k) { return (size_t)std::min(E, T * k) * kRec; }
 
 hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, const int32_t* offsets,
                                const int32_t* sorted_pairs, int k, int max_active, const uint16_t* x, int H, int I,
@@ -549,18 +633,15 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
 }
 
 template <int FMT, int NT>
-static void launch_all(const LayerArgs& a, int max_active, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_layer_route_shared<FMT, NT>), dim3(a.nR + a.nS), dim3(256), lds, s, a);
-  hipLaunchKernelGGL((k_layer_gateup<FMT, NT>), dim3(max_active * a.slices_r), dim3(256), lds, s, a);
-  const int units = max_active + (a.sgate.codes ? 1 : 0);
-  hipLaunchKernelGGL((k_layer_down_combine<FMT, NT>), dim3(units * a.slices_d), dim3(256), lds, s, a);
+static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
+  hipLaunchKernelGGL((k_layer_route_shared<FMT, NT>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s, a);
+  hipLaunchKernelGGL((k_layer_gateup<FMT, NT>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
+  hipLaunchKernelGGL((k_layer_down_combine<FMT, NT>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256), lds.down,
+                     s, a);
 }
 
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                               uint16_t* y, int* sync, float* logits, int32_t* ids, float* w, int32_t* offsets,
-                               int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active, uint16_t* h_routed,
-                               uint16_t* h_shared, float* o_routed, float* o_shared, int32_t* ids_out, float* w_out,
-                               hipStream_t s) {
+                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s) {
   LayerArgs a;
   a.T = T;
   a.H = L->H;
@@ -582,40 +663,41 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   } else {
     a.sgate = a.sup = a.sdown = MatDev{nullptr, nullptr, nullptr, nullptr, 0, 64};
   }
-  a.sync = sync;
-  a.logits = logits;
-  a.ids = ids;
-  a.w = w;
-  a.offsets = offsets;
-  a.sorted_pairs = sorted_pairs;
-  a.pair_pos = pair_pos;
-  a.active = active;
-  a.h_routed = h_routed;
-  a.h_shared = h_shared;
-  a.o_routed = o_routed;
-  a.o_shared = o_shared;
+  a.sync = b.sync;
+  a.logits = b.logits;
+  a.ids = b.ids;
+  a.w = b.w;
+  a.pair_pos = b.pair_pos;
+  a.n_active = b.n_active;
+  a.rec = b.rec;
+  a.h_routed = b.h_routed;
+  a.h_shared = b.h_shared;
+  a.o_routed = b.o_routed;
+  a.o_shared = b.o_shared;
   a.ids_out = ids_out;
   a.w_out = w_out;
-  const int max_active = std::min(a.E, T * a.k);
-  a.nR = (a.E + 3) / 4;
-  a.nS = L->shared ? (a.Is + kRG - 1) / kRG : 0;
-  a.slices_r = (a.I + kRG - 1) / kRG;
-  a.slices_d = (a.H + kRD - 1) / kRD;
+  const int NT = layer_nt(T);
+  a.max_active = std::min(a.E, T * a.k);
+  a.rt = router_tokens(T);
+  a.nRe = (a.E + 3) / 4;
+  a.nR = a.nRe * ((T + a.rt - 1) / a.rt);
+  a.nsb = L->shared ? (T + NT - 1) / NT : 0;
+  // a single token has little work per block: smaller slices spread it over more CUs
+  a.rg = T == 1 ? 4 : kRG;
+  a.rd = T == 1 ? kRDMin : kRD;
+  a.ss_r = L->shared ? (a.Is + a.rg - 1) / a.rg : 0;
+  a.slices_r = (a.I + a.rg - 1) / a.rg;
+  a.slices_d = (a.H + a.rd - 1) / a.rd;
   a.lpr_h = lanes_per_row(a.H);
   a.lpr_i = lanes_per_row(a.I);
   a.lpr_is = a.Is ? lanes_per_row(a.Is) : 64;
-  const size_t lds = layer_decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
+  a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
+  const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const bool nv = L->experts.gate.fmt == kFmtNvfp4;
-  switch (layer_nt(T)) {
-    case 1:
-      nv ? launch_all<kFmtNvfp4, 1>(a, max_active, lds, s) : launch_all<kFmtInt4, 1>(a, max_active, lds, s);
-      break;
-    case 4:
-      nv ? launch_all<kFmtNvfp4, 4>(a, max_active, lds, s) : launch_all<kFmtInt4, 4>(a, max_active, lds, s);
-      break;
-    default:
-      nv ? launch_all<kFmtNvfp4, 8>(a, max_active, lds, s) : launch_all<kFmtInt4, 8>(a, max_active, lds, s);
-  }
+  if (NT == 1)
+    nv ? launch_all<kFmtNvfp4, 1>(a, lds, s) : launch_all<kFmtInt4, 1>(a, lds, s);
+  else
+    nv ? launch_all<kFmtNvfp4, 4>(a, lds, s) : launch_all<kFmtInt4, 4>(a, lds, s);
   return hipGetLastError();
 }
 

@@ -29,11 +29,24 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
 
 size_t layer_decode_lds(int T, int H, int I, int Is, int E, int k);
 int layer_decode_sync_words(int H);
+size_t layer_decode_rec_ints(int T, int E, int k);
+
+// Workspace buffers of the three-launch decode layer.
+struct LayerDecodeBufs {
+  int* sync;           // ticket counters, zero before the first call, left zero
+  float* logits;       // [T, E]
+  int32_t* ids;        // [T*k]
+  float* w;            // [T*k]
+  int32_t* pair_pos;   // [T*k]
+  int32_t* n_active;   // [1]
+  int32_t* rec;        // [layer_decode_rec_ints]
+  uint16_t* h_routed;  // [T*k, I]
+  uint16_t* h_shared;  // [T, Is]
+  float* o_routed;     // [T*k, H]
+  float* o_shared;     // [T, H]
+};
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                               uint16_t* y, int* sync, float* logits, int32_t* ids, float* w, int32_t* offsets,
-                               int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active, uint16_t* h_routed,
-                               uint16_t* h_shared, float* o_routed, float* o_shared, int32_t* ids_out, float* w_out,
-                               hipStream_t s);
+                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s);
 
 size_t mfma_ws_bytes(int E, int H, int I, int total_rows);
 bool mfma_shape_ok(int H, int I);

@@ -7,21 +7,147 @@
 
 namespace moe {
 
-// Top-k of one row of E <= 64*PER logits and softmax over the selection.
-// Every logit becomes a 64-bit key (order-preserving fp32 bits, then
-// 1024 - index) so one unsigned maximum ranks by (larger logit, lower
-// index); k rounds of a DPP wave maximum pick the winners in rank order.
-// Lane 0 writes ids_out[0..k) and w_out[0..k).
-template <int PER, bool COH = false>
+// Router logits of one expert (one wave) against nt <= RT tokens staged in
+// LDS as bf16 rows of H (token t at xs + t*H, H % 4 == 0): fp32 products
+// accumulated per lane in ascending column order, then one fixed-order wave
+// reduction; lane 63 holds acc[t].  Both router kernels use this, so they
+// produce identical bits.
+constexpr int kRouterC = 8;  // float4 router loads in flight per lane
+
+// Load a wave's first kRouterC float4 of router row `wrow` (lane l takes
+// float4 l, l+64, ...): issued before the tokens are staged.
+MOE_DEV void router_prefetch(const float* __restrict__ wrow, int H, int lane, float4 (&wv)[kRouterC]) {
+  const float4* wr = (const float4*)wrow;
+  const int nc = H / 4;
+#pragma unroll
+  for (int q = 0; q < kRouterC; ++q) {
+    const int c = lane + 64 * q;
+    wv[q] = c < nc ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int RT>
+MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restrict__ xs, int H, int nt, int lane,
+                         float (&acc)[RT], float4 (&wv)[kRouterC]) {
+  const float4* wr = (const float4*)wrow;
+  const uint2* xv2 = (const uint2*)xs;
+  const int nc = H / 4;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = 0.f;
+  for (int cb = 0; cb < nc; cb += 64 * kRouterC) {
+    if (cb > 0) {
+#pragma unroll
+      for (int q = 0; q < kRouterC; ++q) {
+        const int c = cb + lane + 64 * q;
+        wv[q] = c < nc ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if (t < nt) {
+#pragma unroll
+        for (int q = 0; q < kRouterC; ++q) {
+          const int c = cb + lane + 64 * q;
+          if (c < nc) {
+            const uint2 v = xv2[t * nc + c];
+            float a = acc[t];
+            a = fmaf(wv[q].x, bf16_to_f32(v.x & 0xffffu), a);
+            a = fmaf(wv[q].y, bf16_to_f32(v.x >> 16), a);
+            a = fmaf(wv[q].z, bf16_to_f32(v.y & 0xffffu), a);
+            a = fmaf(wv[q].w, bf16_to_f32(v.y >> 16), a);
+            acc[t] = a;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+    if (t < nt) acc[t] = group_sum_last<64>(acc[t]);
+}
+
+// Copy n16 16-byte chunks from global to LDS, eight loads in flight per
+// thread before the stores (named registers, not an array, so nothing goes
+// through private memory).
+MOE_DEV void copy_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16) {
+  const int nthr = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < n16; i0 += 8 * nthr) {
+    const int i1 = i0 + nthr, i2 = i0 + 2 * nthr, i3 = i0 + 3 * nthr;
+    const int i4 = i0 + 4 * nthr, i5 = i0 + 5 * nthr, i6 = i0 + 6 * nthr, i7 = i0 + 7 * nthr;
+    uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+    v0 = src[i0];
+    if (i1 < n16) v1 = src[i1];
+    if (i2 < n16) v2 = src[i2];
+    if (i3 < n16) v3 = src[i3];
+    if (i4 < n16) v4 = src[i4];
+    if (i5 < n16) v5 = src[i5];
+    if (i6 < n16) v6 = src[i6];
+    if (i7 < n16) v7 = src[i7];
+    dst[i0] = v0;
+    if (i1 < n16) dst[i1] = v1;
+    if (i2 < n16) dst[i2] = v2;
+    if (i3 < n16) dst[i3] = v3;
+    if (i4 < n16) dst[i4] = v4;
+    if (i5 < n16) dst[i5] = v5;
+    if (i6 < n16) dst[i6] = v6;
+    if (i7 < n16) dst[i7] = v7;
+  }
+}
+
+// Copy n floats from global to LDS, eight loads in flight per thread.
+MOE_DEV void copy_f32_to_lds(float* __restrict__ dst, const float* __restrict__ src, int n) {
+  const int nthr = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * nthr) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + u * nthr < n ? src[i0 + u * nthr] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * nthr < n) dst[i0 + u * nthr] = v[u];
+  }
+}
+
+// Maximum of a float over the wave, in every lane: inclusive max-scan with
+// row_shr 1, 2, 3, 4, 8 and row_bcast 15, 31 (lanes without a source keep
+// their own value), then lane 63 is broadcast.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+MOE_DEV float dpp_keep_f32(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, ROW_MASK, BANK_MASK, false));
+}
+MOE_DEV float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_keep_f32<0x111, 0xf, 0xf>(v));
+  v = fmaxf(v, dpp_keep_f32<0x112, 0xf, 0xf>(v));
+  v = fmaxf(v, dpp_keep_f32<0x113, 0xf, 0xf>(v));
+  v = fmaxf(v, dpp_keep_f32<0x114, 0xf, 0xe>(v));
+  v = fmaxf(v, dpp_keep_f32<0x118, 0xf, 0xc>(v));
+  v = fmaxf(v, dpp_keep_f32<0x142, 0xa, 0xf>(v));
+  v = fmaxf(v, dpp_keep_f32<0x143, 0xc, 0xf>(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Top-k of one row of E <= 64*PER logits (lane l holds experts i*64 + l)
+// and softmax over the selection.  Each of the k rounds takes the wave
+// maximum of the remaining values, then the lowest expert index holding it
+// (ballots in ascending index order), so ties go to the lower index; -0 and
+// +0 compare equal.  NaN logits never win over a number; once only NaN
+// remain, the lowest unselected index is taken, so the k ids are always
+// distinct and in [0, E) whatever the values.  Lane 0 writes ids_out[0..k)
+// and w_out[0..k).
+template <int PER>
 MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, int lane, int32_t* ids_out,
                                  float* w_out) {
-  uint64_t key[PER];
+  float v[PER];
+  uint32_t inr = 0, num = 0;  // bit i: expert i*64 + lane exists / holds a number (not NaN)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = i * 64 + lane;
-    const float v = e < E ? (COH ? ld_dev(row + e) : row[e]) : 0.f;
-    key[i] = e < E ? (((uint64_t)f32_order_key(v) << 32) | (uint32_t)(1024 - e)) : 0ull;
+    const float x = e < E ? row[e] : 0.f;
+    v[i] = x;
+    inr |= e < E ? (1u << i) : 0u;
+    num |= (e < E && x == x) ? (1u << i) : 0u;
   }
+  uint32_t taken = 0;
   float sv[8];
   int se[8];
 #pragma unroll
@@ -29,18 +155,25 @@ MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, in
     sv[j] = 0.f;
     se[j] = 0;
     if (j < k) {
-      uint64_t m = 0;
+      const uint32_t cand = num & ~taken;
+      float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) m = max_u64(m, key[i]);
-      m = wave_max_u64(m);
-      const int e = 1024 - (int)(uint32_t)m;
-      sv[j] = f32_from_order_key((uint32_t)(m >> 32));
-      se[j] = e;
-      if ((e & 63) == lane) {
+      for (int i = 0; i < PER; ++i) m = fmaxf(m, (cand >> i) & 1u ? v[i] : -INFINITY);
+      m = wave_max_f32(m);
+      int e = -1;
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (i == (e >> 6)) key[i] = 0ull;
+      for (int i = 0; i < PER; ++i) {
+        const uint64_t b = __ballot(((cand >> i) & 1u) && v[i] == m);
+        if (e < 0 && b) e = i * 64 + (int)__builtin_ctzll(b);
       }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {  // only NaN left: lowest unselected index
+        const uint64_t b = __ballot(((inr & ~taken) >> i) & 1u);
+        if (e < 0 && b) e = i * 64 + (int)__builtin_ctzll(b);
+      }
+      sv[j] = m;
+      se[j] = e;
+      if ((e & 63) == lane) taken |= 1u << (e >> 6);
     }
   }
   if (lane == 0) {
@@ -63,16 +196,13 @@ MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, in
   }
 }
 
-// COH: read the logits with device-coherent loads (they were written by
-// other blocks of the same launch).
-template <bool COH = false>
 MOE_DEV void wave_topk_softmax(const float* __restrict__ row, int E, int k, int lane, int32_t* ids_out,
                                float* w_out) {
-  if (E <= 64) wave_topk_softmax_t<1, COH>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 128) wave_topk_softmax_t<2, COH>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 256) wave_topk_softmax_t<4, COH>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 512) wave_topk_softmax_t<8, COH>(row, E, k, lane, ids_out, w_out);
-  else wave_topk_softmax_t<16, COH>(row, E, k, lane, ids_out, w_out);
+  if (E <= 64) wave_topk_softmax_t<1>(row, E, k, lane, ids_out, w_out);
+  else if (E <= 128) wave_topk_softmax_t<2>(row, E, k, lane, ids_out, w_out);
+  else if (E <= 256) wave_topk_softmax_t<4>(row, E, k, lane, ids_out, w_out);
+  else if (E <= 512) wave_topk_softmax_t<8>(row, E, k, lane, ids_out, w_out);
+  else wave_topk_softmax_t<16>(row, E, k, lane, ids_out, w_out);
 }
 
 // Exclusive prefix sum over a block of up to 1024 threads (all threads must

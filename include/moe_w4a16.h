@@ -170,10 +170,10 @@ int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* top
  * composing moe_route, moe_permute, moe_grouped_w4a16_ffn and moe_combine.
  * residual bf16 [T, H] may be NULL; y bf16 [T, H]; ids_out int32 [T, k] and
  * w_out fp32 [T, k] may be NULL.  Workspace: moe_layer_decode_workspace_size
- * bytes, 256-byte aligned, ZERO-FILLED before its first use: it starts
- * with ticket counters (int32 word 0 and words 16*(1+s) for each 64-row
- * slice s of H) that the decode kernels use to hand work to the last block
- * of a group; every call leaves them reset.  Calls sharing a
+ * bytes, 256-byte aligned, ZERO-FILLED before its first use: its first
+ * 64 * (17 + ceil(H / 32)) bytes hold int32 ticket counters that the decode
+ * kernels use to hand work to the last block of a group; every call leaves
+ * them reset to zero.  Calls sharing a
  * workspace must not run concurrently.  The shared expert must have the
  * same format and hidden size as the routed experts. */
 size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T);

@@ -66,6 +66,18 @@ def test_topk_adversarial_cases():
     assert oracle.topk_select(np.arange(E, dtype=float)[None], E)[0].tolist() == list(range(E - 1, -1, -1))
 
 
+def test_topk_non_finite_order():
+    """Non-finite logits (the pages are silent): +inf ranks first, -inf below every
+    finite value, NaN below everything; ties and NaNs go to the lower index, so the
+    k ids are always distinct and in range."""
+    nan, inf = float("nan"), float("inf")
+    row = [1.0, nan, -inf, 3.0, inf, nan, -2.0, 3.0]
+    assert oracle.topk_select(np.array([row]), 8)[0].tolist() == [4, 3, 7, 0, 6, 2, 1, 5]
+    assert oracle.topk_select(np.full((1, 5), nan), 3)[0].tolist() == [0, 1, 2]
+    both = [nan, -inf, nan, -inf]
+    assert oracle.topk_select(np.array([both]), 4)[0].tolist() == [1, 3, 0, 2]
+
+
 def test_weights_sum_to_one_and_are_ordered():
     rng = np.random.default_rng(2)
     T, E, k = 2000, 256, 6

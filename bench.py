@@ -9,8 +9,9 @@ copies (more than twice the size of the on-die caches) and fresh tokens, so
 weights stream from HBM; K steps are captured in one HIP graph and replayed.
 
 Other workloads (--workload): decode batch sweep (decode_T4, decode_T16,
-decode_T64, with --fmt int4), the 47-layer batch-8 chain (chain_b8) and the
-4096-token prefill (prefill).
+decode_T64, with --fmt int4), the 47-layer batch-8 chain (chain_b8), the
+4096-token prefill (prefill), and hbm_copy: a plain 1 GiB device copy whose
+HBM counter readings calibrate the traffic figures of the others.
 
 Prints ONE JSON line (rank 0).
 """
@@ -60,6 +61,8 @@ def main():
         return bench_prefill(args, fmt)
     if workload == "chain_b8":
         return bench_chain(args, fmt)
+    if workload == "hbm_copy":
+        return bench_copy(args)
     T = {"decode_b1": 1, "decode_T4": 4, "decode_T16": 16, "decode_T64": 64}.get(workload)
     if T is None:
         print("unknown workload %s" % workload, file=sys.stderr)
@@ -181,26 +184,66 @@ def main():
     print(json.dumps(out))
 
 
-def timed_graph(torch, stream, body, K, W):
-    """Warm up W eager steps, capture K steps in one graph, time one replay."""
+def timed_graph(torch, stream, body, K, W, use_graph=True):
+    """Warm up W eager steps, capture K steps in one graph, time one replay
+    (or, without a graph, time K eager steps)."""
     with torch.cuda.stream(stream):
         for i in range(W):
             body(i, stream)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(K):
-            body(i, stream)
-    graph.replay()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                body(i, stream)
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                body(i, stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)
+
+
+def bench_copy(args):
+    """A plain device copy of 1 GiB (torch's copy kernel): 1 GiB read + 1 GiB written per step."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    stream = torch.cuda.Stream()
+    for _ in range(W):
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        graph.replay()
+        for _ in range(K):
+            dst.copy_(src)
         ev1.record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1)
+    ms = ev0.elapsed_time(ev1)
+    gbs = 2.0 * n * K / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+                      "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+                      "config": {"workload": "hbm_copy 1 GiB", "bytes_read_per_step": n,
+                                 "bytes_written_per_step": n},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "torch copy"},
+                      "cpu_baseline": None}))
 
 
 def bench_prefill(args, fmt):
@@ -246,14 +289,14 @@ def bench_prefill(args, fmt):
         moe.moe_combine(out, pp, w, out_s, x, T, k, H, y, stream=s)
 
     stream = torch.cuda.Stream()
-    ms = timed_graph(torch, stream, step, K, W)
+    ms = timed_graph(torch, stream, step, K, W, not args.no_graph)
     # the grouped FFN alone (routed + shared), timed the same way
     def ffn_only(i, s):
         moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
                                   gws_n, stream=s)
         moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws,
                                   gws_n, stream=s)
-    ms_ffn = timed_graph(torch, stream, ffn_only, K, W)
+    ms_ffn = timed_graph(torch, stream, ffn_only, K, W, not args.no_graph)
     flops = 6.0 * (n + T) * H * I
     c = counts.cpu().numpy()
     out_line = {

@@ -20,7 +20,10 @@
 // (B) l % 32 and 8 consecutive k values; the accumulator register i of lane l
 // holds row (i / 4) * 8 + (l / 32) * 4 + i % 4, column l % 32.
 // LDS tiles are [128 rows][64 k] bf16 with the 16-byte chunk index XOR-ed by
-// (row >> 1) & 7, so the 16 lanes of an LDS pass hit distinct banks.
+// row & 7: a 128-byte row spans all 32 banks, so the 8 lanes that one LDS
+// cycle serves for a 16-byte access (8 consecutive rows at one chunk, or 4
+// rows at chunks c and c + 4) land on distinct banks.  Two tile buffers
+// alternate between K steps, so each step needs one barrier.
 #include "common.cuh"
 #include "launch.h"
 #include "route.cuh"
@@ -47,11 +50,19 @@ struct MfmaArgs {
   float* out;                   // [rows, H]
 };
 
-MOE_DEV int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }  // in 16-byte units
+MOE_DEV int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }  // in 16-byte units
 
 // Dequantise 32 consecutive weights (16 bytes of codes) of one row into 4
 // bf16 chunks of 8.  NVFP4: two e4m3 block scales (bytes 0, 1 of `sc`).
-// INT4: zero point z; the result is the exact integer q - z.
+// INT4: zero point z; the result is the exact integer q - z.  Every value is
+// exact in fp32 and in bf16, so the hardware fp32 -> bf16 conversion does
+// not round.
+MOE_DEV uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int FMT>
 MOE_DEV void dequant32(uint4 c, uint32_t sc, int z, uint4 (&o)[4]) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -65,14 +76,15 @@ MOE_DEV void dequant32(uint4 c, uint32_t sc, int z, uint4 (&o)[4]) {
       v[0] = p0.x * b; v[1] = p0.y * b; v[2] = p1.x * b; v[3] = p1.y * b;
       v[4] = p2.x * b; v[5] = p2.y * b; v[6] = p3.x * b; v[7] = p3.y * b;
     } else {
+      // 2^23 + q as fp32 bits, minus 2^23 + z: exact
+      const float off = 8388608.0f + (float)z;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (float)((int)((w[q] >> (4 * j)) & 15u) - z);
+      for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(0x4B000000u | ((w[q] >> (4 * j)) & 15u)) - off;
     }
-    // exact values: the conversion to bf16 does not round
-    o[q].x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    o[q].y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-    o[q].z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-    o[q].w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+    o[q].x = pack_bf16(v[0], v[1]);
+    o[q].y = pack_bf16(v[2], v[3]);
+    o[q].z = pack_bf16(v[4], v[5]);
+    o[q].w = pack_bf16(v[6], v[7]);
   }
 }
 
@@ -113,17 +125,44 @@ __global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__
   if (e == 0) tiles[0] = total;
 }
 
+// One K step's global data for this thread, loaded two steps ahead of its
+// use (two register sets in turn) so that the memory latency is covered by
+// the matrix work of the steps in between.
+struct MfmaStage {
+  uint4 a[4];      // 4 x 8 bf16 of one activation row
+  uint4 b;         // 32 packed 4-bit weights of one weight row
+  uint32_t sc;     // NVFP4: the two e4m3 block scales of those 32 weights
+  int z;           // INT4: zero point of this K step's group
+  float s0, s1;    // INT4: this wave's two per-column group scales (fp16 -> fp32)
+};
+
+// Map the block index to (row tile, column slice) so that every column slice
+// of a row tile runs on the same XCD (blocks go to XCDs round-robin), and the
+// tile's activation rows stay in that XCD's L2.
+MOE_DEV void block_tile(int nslices, int& tile, int& slice) {
+#ifdef MOE_EXP_NO_XCD
+  tile = blockIdx.x % (gridDim.x / nslices);
+  slice = blockIdx.x / (gridDim.x / nslices);
+#else
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  tile = (j / nslices) * 8 + xcd;
+  slice = j % nslices;
+#endif
+}
+
 // ------------------------------------------------------------------ gate/up
 // Block: 4 waves as 2 (rows) x 2 (features); each wave owns a 64-row x 32-
 // feature tile of both G and U (2 x 2 accumulators of 32 x 32).
 template <int FMT>
 __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
-  __shared__ uint4 As[kBM * 8];  // [128][64] bf16, swizzled
-  __shared__ uint4 Bs[128 * 8];  // rows 0..63 gate, 64..127 up
+  __shared__ uint4 As2[2][kBM * 8];  // [128][64] bf16, swizzled
+  __shared__ uint4 Bs2[2][128 * 8];  // rows 0..63 gate, 64..127 up
+  int tile, slice;
+  block_tile(g.I / 64, tile, slice);
   int e, r0, r1;
-  if (!tile_of(g, blockIdx.x, e, r0, r1)) return;
+  if (!tile_of(g, tile, e, r0, r1)) return;
   const int H = g.H, I = g.I;
-  const int n0 = blockIdx.y * 64;
+  const int n0 = slice * 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   // loader roles: A row tid >> 1, 4 chunks from (tid & 1) * 4; B matrix tid >> 7, row (tid >> 1) & 63, half tid & 1
@@ -136,6 +175,10 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
   const uint8_t* bcodes = (b_mat ? g.uc : g.gc) + wrow * (H / 2) + b_half * 16;
   const uint8_t* bscales = b_mat ? g.us : g.gs;
   const uint8_t* bzeros = b_mat ? g.uz : g.gz;
+  // this wave's gate / up feature column (INT4 group scales)
+  const int ncol = n0 + wn * 32 + (lane & 31);
+  const uint16_t* gsc = (const uint16_t*)g.gs + ((size_t)e * I + ncol) * (H / 64);
+  const uint16_t* usc = (const uint16_t*)g.us + ((size_t)e * I + ncol) * (H / 64);
 
   f32x16_t acc[2][2];  // [gate / up][row sub-tile]
 #pragma unroll
@@ -144,46 +187,39 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
     for (int m = 0; m < 2; ++m) acc[a][m] = f32x16_t{};
 
   const int nk = H / kBK;
-  uint4 ra[4], rb;
-  uint32_t rsc = 0;
-  int rz = 0;
-  auto load = [&](int kt) {
+  auto load = [&](int kt, MfmaStage& st) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      ra[c] = a_valid ? ((const uint4*)(xrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
-    rb = *(const uint4*)(bcodes + kt * (kBK / 2));
+      st.a[c] = a_valid ? ((const uint4*)(xrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
+    st.b = *(const uint4*)(bcodes + kt * (kBK / 2));
     if (FMT == kFmtNvfp4) {
-      rsc = *(const uint16_t*)(bscales + wrow * (H / 16) + kt * 4 + b_half * 2);
+      st.sc = *(const uint16_t*)(bscales + wrow * (H / 16) + kt * 4 + b_half * 2);
     } else {
-      rsc = 0;
-      rz = bzeros[wrow * (H / 64) + kt];
+      st.z = bzeros[wrow * (H / 64) + kt];
+      st.s0 = f16_to_f32(gsc[kt]);
+      st.s1 = f16_to_f32(usc[kt]);
     }
   };
-  // per-lane INT4 group scales of this wave's gate / up feature column
-  const int ncol = n0 + wn * 32 + (lane & 31);
-  load(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
+  // Write this K step's tiles into buffer `buf`.  The buffer was last read
+  // two steps ago, before every wave passed the previous step's barrier.
+  auto step = [&](const MfmaStage& st, int buf) {
+    uint4* As = As2[buf];
+    uint4* Bs = Bs2[buf];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = ra[c];
+    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = st.a[c];
     {
       uint4 o[4];
-      dequant32<FMT>(rb, rsc, rz, o);
+      dequant32<FMT>(st.b, st.sc, st.z, o);
 #pragma unroll
       for (int c = 0; c < 4; ++c) Bs[swz(b_mat * 64 + b_row, b_half * 4 + c)] = o[c];
     }
     __syncthreads();
-    float sg = 1.f, su = 1.f;
-    if (FMT == kFmtInt4) {
-      sg = f16_to_f32(((const uint16_t*)g.gs)[((size_t)e * I + ncol) * (H / 64) + kt]);
-      su = f16_to_f32(((const uint16_t*)g.us)[((size_t)e * I + ncol) * (H / 64) + kt]);
-    }
-    if (kt + 1 < nk) load(kt + 1);
-    f32x16_t part[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) part[a][m] = (FMT == kFmtInt4) ? f32x16_t{} : acc[a][m];
+  };
+  // NVFP4 accumulates straight into acc; INT4 accumulates one group in part
+  // and adds it to acc times the group's scale.
+  auto mma = [&](f32x16_t (&c)[2][2], int buf) {
+    const uint4* As = As2[buf];
+    const uint4* Bs = Bs2[buf];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -191,24 +227,49 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
       const bf16x8_t a1 = lds_frag(As, wm * 64 + 32 + (lane & 31), chunk);
       const bf16x8_t bg = lds_frag(Bs, wn * 32 + (lane & 31), chunk);
       const bf16x8_t bu = lds_frag(Bs, 64 + wn * 32 + (lane & 31), chunk);
-      part[0][0] = mfma(a0, bg, part[0][0]);
-      part[0][1] = mfma(a1, bg, part[0][1]);
-      part[1][0] = mfma(a0, bu, part[1][0]);
-      part[1][1] = mfma(a1, bu, part[1][1]);
+      c[0][0] = mfma(a0, bg, c[0][0]);
+      c[0][1] = mfma(a1, bg, c[0][1]);
+      c[1][0] = mfma(a0, bu, c[1][0]);
+      c[1][1] = mfma(a1, bu, c[1][1]);
     }
+  };
+  auto compute = [&](float sg, float su, int buf) {
+    if (FMT == kFmtNvfp4) {
+      mma(acc, buf);
+    } else {
+      f32x16_t part[2][2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (FMT == kFmtInt4) {
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) part[a][m] = f32x16_t{};
+      mma(part, buf);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           acc[0][m][i] = fmaf(sg, part[0][m][i], acc[0][m][i]);
           acc[1][m][i] = fmaf(su, part[1][m][i], acc[1][m][i]);
         }
-      } else {
-        acc[0][m] = part[0][m];
-        acc[1][m] = part[1][m];
       }
     }
+  };
+  MfmaStage s0, s1;
+  load(0, s0);
+  if (nk > 1) load(1, s1);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(s0, 0);
+    const float q0 = s0.s0, q1 = s0.s1;
+    if (kt + 2 < nk) load(kt + 2, s0);
+    compute(q0, q1, 0);
+    step(s1, 1);
+    const float p0 = s1.s0, p1 = s1.s1;
+    if (kt + 3 < nk) load(kt + 3, s1);
+    compute(p0, p1, 1);
+  }
+  if (kt < nk) {  // odd number of K steps
+    step(s0, 0);
+    compute(s0.s0, s0.s1, 0);
   }
   // epilogue: h = bf16(silu(ts_g * G) * (ts_u * U))
   const float tsg = FMT == kFmtNvfp4 ? g.gts[e] : 1.f, tsu = FMT == kFmtNvfp4 ? g.uts[e] : 1.f;
@@ -229,12 +290,14 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
 // Block: 4 waves as 2 x 2, each a 64-row x 64-column tile (2 x 2 accumulators).
 template <int FMT>
 __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
-  __shared__ uint4 As[kBM * 8];
-  __shared__ uint4 Bs[128 * 8];
+  __shared__ uint4 As2[2][kBM * 8];
+  __shared__ uint4 Bs2[2][128 * 8];
+  int tile, slice;
+  block_tile(g.H / 128, tile, slice);
   int e, r0, r1;
-  if (!tile_of(g, blockIdx.x, e, r0, r1)) return;
+  if (!tile_of(g, tile, e, r0, r1)) return;
   const int H = g.H, I = g.I;
-  const int n0 = blockIdx.y * 128;
+  const int n0 = slice * 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int a_row = tid >> 1, a_c0 = (tid & 1) * 4;
@@ -243,6 +306,9 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
   const int b_row = tid >> 1, b_half = tid & 1;
   const size_t wrow = (size_t)e * H + n0 + b_row;
   const uint8_t* bcodes = g.dc + wrow * (I / 2) + b_half * 16;
+  const int ncol0 = n0 + wn * 64 + (lane & 31);
+  const uint16_t* dsc0 = (const uint16_t*)g.ds + ((size_t)e * H + ncol0) * (I / 64);
+  const uint16_t* dsc1 = (const uint16_t*)g.ds + ((size_t)e * H + ncol0 + 32) * (I / 64);
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -250,44 +316,35 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x16_t{};
   const int nk = I / kBK;
-  uint4 ra[4], rb;
-  uint32_t rsc = 0;
-  int rz = 0;
-  auto load = [&](int kt) {
+  auto load = [&](int kt, MfmaStage& st) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      ra[c] = a_valid ? ((const uint4*)(hrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
-    rb = *(const uint4*)(bcodes + kt * (kBK / 2));
+      st.a[c] = a_valid ? ((const uint4*)(hrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
+    st.b = *(const uint4*)(bcodes + kt * (kBK / 2));
     if (FMT == kFmtNvfp4) {
-      rsc = *(const uint16_t*)(g.ds + wrow * (I / 16) + kt * 4 + b_half * 2);
+      st.sc = *(const uint16_t*)(g.ds + wrow * (I / 16) + kt * 4 + b_half * 2);
     } else {
-      rz = g.dz[wrow * (I / 64) + kt];
+      st.z = g.dz[wrow * (I / 64) + kt];
+      st.s0 = f16_to_f32(dsc0[kt]);
+      st.s1 = f16_to_f32(dsc1[kt]);
     }
   };
-  const int ncol0 = n0 + wn * 64 + (lane & 31);
-  load(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
+  auto step = [&](const MfmaStage& st, int buf) {
+    uint4* As = As2[buf];
+    uint4* Bs = Bs2[buf];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = ra[c];
+    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = st.a[c];
     {
       uint4 o[4];
-      dequant32<FMT>(rb, rsc, rz, o);
+      dequant32<FMT>(st.b, st.sc, st.z, o);
 #pragma unroll
       for (int c = 0; c < 4; ++c) Bs[swz(b_row, b_half * 4 + c)] = o[c];
     }
     __syncthreads();
-    float s0 = 1.f, s1 = 1.f;
-    if (FMT == kFmtInt4) {
-      s0 = f16_to_f32(((const uint16_t*)g.ds)[((size_t)e * H + ncol0) * (I / 64) + kt]);
-      s1 = f16_to_f32(((const uint16_t*)g.ds)[((size_t)e * H + ncol0 + 32) * (I / 64) + kt]);
-    }
-    if (kt + 1 < nk) load(kt + 1);
-    f32x16_t part[2][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) part[m][n] = (FMT == kFmtInt4) ? f32x16_t{} : acc[m][n];
+  };
+  auto mma = [&](f32x16_t (&c)[2][2], int buf) {
+    const uint4* As = As2[buf];
+    const uint4* Bs = Bs2[buf];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -295,24 +352,49 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
       const bf16x8_t a1 = lds_frag(As, wm * 64 + 32 + (lane & 31), chunk);
       const bf16x8_t b0 = lds_frag(Bs, wn * 64 + (lane & 31), chunk);
       const bf16x8_t b1 = lds_frag(Bs, wn * 64 + 32 + (lane & 31), chunk);
-      part[0][0] = mfma(a0, b0, part[0][0]);
-      part[0][1] = mfma(a0, b1, part[0][1]);
-      part[1][0] = mfma(a1, b0, part[1][0]);
-      part[1][1] = mfma(a1, b1, part[1][1]);
+      c[0][0] = mfma(a0, b0, c[0][0]);
+      c[0][1] = mfma(a0, b1, c[0][1]);
+      c[1][0] = mfma(a1, b0, c[1][0]);
+      c[1][1] = mfma(a1, b1, c[1][1]);
     }
+  };
+  auto compute = [&](float s0, float s1, int buf) {
+    if (FMT == kFmtNvfp4) {
+      mma(acc, buf);
+    } else {
+      f32x16_t part[2][2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (FMT == kFmtInt4) {
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) part[m][n] = f32x16_t{};
+      mma(part, buf);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           acc[m][0][i] = fmaf(s0, part[m][0][i], acc[m][0][i]);
           acc[m][1][i] = fmaf(s1, part[m][1][i], acc[m][1][i]);
         }
-      } else {
-        acc[m][0] = part[m][0];
-        acc[m][1] = part[m][1];
       }
     }
+  };
+  MfmaStage s0, s1;
+  load(0, s0);
+  if (nk > 1) load(1, s1);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(s0, 0);
+    const float q0 = s0.s0, q1 = s0.s1;
+    if (kt + 2 < nk) load(kt + 2, s0);
+    compute(q0, q1, 0);
+    step(s1, 1);
+    const float p0 = s1.s0, p1 = s1.s1;
+    if (kt + 3 < nk) load(kt + 3, s1);
+    compute(p0, p1, 1);
+  }
+  if (kt < nk) {  // odd number of K steps
+    step(s0, 0);
+    compute(s0.s0, s0.s1, 0);
   }
   const float ts = FMT == kFmtNvfp4 ? g.dts[e] : 1.f;
 #pragma unroll
@@ -368,7 +450,9 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.h = h;
   g.out = out;
   hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, tiles);
-  const dim3 ga((unsigned)max_tiles, I / 64), gd((unsigned)max_tiles, H / 128);
+  // one block per (row tile, column slice); tiles rounded up to a multiple of the 8 XCDs
+  const unsigned tiles8 = (unsigned)((max_tiles + 7) / 8 * 8);
+  const dim3 ga(tiles8 * (I / 64)), gd(tiles8 * (H / 128));
   if (w->gate.fmt == kFmtNvfp4) {
     hipLaunchKernelGGL(k_mfma_gateup<kFmtNvfp4>, ga, dim3(256), 0, s, g);
     hipLaunchKernelGGL(k_mfma_down<kFmtNvfp4>, gd, dim3(256), 0, s, g);

@@ -320,9 +320,14 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   unsigned long long* mask = (unsigned long long*)(((uintptr_t)(s_log + kRouteT * E) + 7) & ~(uintptr_t)7);  // [E]
   int32_t* off = (int32_t*)(mask + E);                                  // [E + 1]
   int* scan_tmp = (int*)(off + E + 1);                                  // [17]
+  float* cand_v = (float*)(scan_tmp + 17);                              // [4 * 8]
+  int32_t* cand_e = (int32_t*)(cand_v + 32);                            // [4 * 8]
   copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
   __syncthreads();
-  if (wave < nt) wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
+  if (nt == 1)  // a lone token: all four waves share its selection
+    block_topk_softmax(s_log, E, k, wave, lane, cand_v, cand_e, s_ids + t0 * k, s_w + t0 * k);
+  else if (wave < nt)
+    wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
   __syncthreads();
   MOE_TRACE_AT(0, 6);
   const int p0 = t0 * k, p1 = (t0 + nt) * k;  // this batch's pairs
@@ -351,6 +356,32 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     }
     __syncthreads();
     MOE_TRACE_AT(0, 7);
+  }
+
+  if (T == 1) {
+    // One token, k distinct experts: each is a unit of one row, and its
+    // record index is its rank among the chosen ids.
+    if (tid < k) {
+      const int ee = s_ids[tid];
+      int rank = 0;
+      for (int j = 0; j < k; ++j) rank += s_ids[j] < ee;
+      int32_t* r = a.rec + (size_t)rank * kRec;
+      r[0] = ee;
+      r[1] = rank;
+      r[2] = 1;
+      r[3] = 0;
+      r[4] = 0;
+      a.pair_pos[tid] = rank;
+      a.ids[tid] = ee;
+      a.w[tid] = s_w[tid];
+      if (a.ids_out) {
+        a.ids_out[tid] = ee;
+        a.w_out[tid] = s_w[tid];
+      }
+    }
+    if (tid == 0) a.n_active[0] = k;
+    MOE_TRACE_AT(0, 4);
+    return;
   }
 
   // Every token's choices are in LDS.  Stable grouping of pairs p = t*k + j
@@ -581,7 +612,8 @@ static DecodeLds decode_lds(int T, int H, int I, int Is, int E, int k) {
   DecodeLds d{0, 0, 0};
   if (T < 1 || T > 64 || E > 1024 || H > 4096) return d;
   const int NT = layer_nt(T);
-  const size_t tables = (size_t)T * k * 8 + (size_t)kRouteT * E * 4 + 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 17 * 4;
+  const size_t tables =
+      (size_t)T * k * 8 + (size_t)kRouteT * E * 4 + 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 17 * 4 + 64 * 4;
   const size_t route = std::max((size_t)router_tokens(T) * H * 2, std::max(tables, stage_bytes(NT, H)));
   const size_t gateup = stage_bytes(NT, H);
   const size_t down = align16(stage_bytes(NT, std::max(I, Is))) + (size_t)T * k * 8;

@@ -140,14 +140,9 @@ struct MfmaStage {
 // of a row tile runs on the same XCD (blocks go to XCDs round-robin), and the
 // tile's activation rows stay in that XCD's L2.
 MOE_DEV void block_tile(int nslices, int& tile, int& slice) {
-#ifdef MOE_EXP_NO_XCD
-  tile = blockIdx.x % (gridDim.x / nslices);
-  slice = blockIdx.x / (gridDim.x / nslices);
-#else
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   tile = (j / nslices) * 8 + xcd;
   slice = j % nslices;
-#endif
 }
 
 // ------------------------------------------------------------------ gate/up

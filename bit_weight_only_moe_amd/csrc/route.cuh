@@ -126,19 +126,17 @@ MOE_DEV float wave_max_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Top-k of one row of E <= 64*PER logits (lane l holds experts i*64 + l)
-// and softmax over the selection.  Each of the k rounds takes the wave
-// maximum of the remaining values, then the lowest expert index holding it
-// (ballots in ascending index order), so ties go to the lower index; -0 and
-// +0 compare equal.  NaN logits never win over a number; once only NaN
-// remain, the lowest unselected index is taken, so the k ids are always
-// distinct and in [0, E) whatever the values.  Lane 0 writes ids_out[0..k)
-// and w_out[0..k).
+// Top-k selection over one row of E <= 64*PER values (lane l holds entries
+// i*64 + l).  Each of the k rounds takes the wave maximum of the remaining
+// values, then the lowest index holding it (ballots in ascending index
+// order), so ties go to the lower index; -0 and +0 compare equal.  NaN never
+// wins over a number; once only NaN remain, the lowest unselected index is
+// taken, so the k indices are always distinct and in [0, E) whatever the
+// values.  sv/se (wave-uniform) receive values and indices in rank order.
 template <int PER>
-MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, int lane, int32_t* ids_out,
-                                 float* w_out) {
+MOE_DEV void wave_topk_select(const float* __restrict__ row, int E, int k, int lane, float (&sv)[8], int (&se)[8]) {
   float v[PER];
-  uint32_t inr = 0, num = 0;  // bit i: expert i*64 + lane exists / holds a number (not NaN)
+  uint32_t inr = 0, num = 0;  // bit i: entry i*64 + lane exists / holds a number (not NaN)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = i * 64 + lane;
@@ -148,8 +146,6 @@ MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, in
     num |= (e < E && x == x) ? (1u << i) : 0u;
   }
   uint32_t taken = 0;
-  float sv[8];
-  int se[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     sv[j] = 0.f;
@@ -176,6 +172,21 @@ MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, in
       if ((e & 63) == lane) taken |= 1u << (e >> 6);
     }
   }
+}
+
+MOE_DEV void wave_topk_select_any(const float* __restrict__ row, int E, int k, int lane, float (&sv)[8],
+                                  int (&se)[8]) {
+  if (E <= 64) wave_topk_select<1>(row, E, k, lane, sv, se);
+  else if (E <= 128) wave_topk_select<2>(row, E, k, lane, sv, se);
+  else if (E <= 256) wave_topk_select<4>(row, E, k, lane, sv, se);
+  else if (E <= 512) wave_topk_select<8>(row, E, k, lane, sv, se);
+  else wave_topk_select<16>(row, E, k, lane, sv, se);
+}
+
+// Softmax over the k selected values (in rank order, sv[0] the largest);
+// lane 0 writes ids_out[0..k) and w_out[0..k).
+MOE_DEV void topk_softmax_write(const float (&sv)[8], const int (&se)[8], int k, int lane, int32_t* ids_out,
+                                float* w_out) {
   if (lane == 0) {
     float ex[8], sum = 0.f;
 #pragma unroll
@@ -196,13 +207,59 @@ MOE_DEV void wave_topk_softmax_t(const float* __restrict__ row, int E, int k, in
   }
 }
 
+// Top-k + softmax of one row of E <= 1024 logits by one wave.
 MOE_DEV void wave_topk_softmax(const float* __restrict__ row, int E, int k, int lane, int32_t* ids_out,
                                float* w_out) {
-  if (E <= 64) wave_topk_softmax_t<1>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 128) wave_topk_softmax_t<2>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 256) wave_topk_softmax_t<4>(row, E, k, lane, ids_out, w_out);
-  else if (E <= 512) wave_topk_softmax_t<8>(row, E, k, lane, ids_out, w_out);
-  else wave_topk_softmax_t<16>(row, E, k, lane, ids_out, w_out);
+  float sv[8];
+  int se[8];
+  wave_topk_select_any(row, E, k, lane, sv, se);
+  topk_softmax_write(sv, se, k, lane, ids_out, w_out);
+}
+
+// Top-k + softmax of one row of E <= 1024 logits (in LDS) by the 4 waves of
+// a block: wave w selects the top min(k, n_w) of its quarter of the row
+// (contiguous index ranges, in ascending order), the candidates are stored
+// in wave order, and wave 0 selects among them.  Within a quarter, tied
+// candidates are in ascending index order and the quarters are ordered, so
+// candidate position order is index order and the result equals the
+// one-wave selection.  cand_v / cand_e: LDS scratch of 4*k entries.  Call
+// from all 4 waves; contains one __syncthreads.
+MOE_DEV void block_topk_softmax(const float* __restrict__ row, int E, int k, int wave, int lane,
+                                float* __restrict__ cand_v, int32_t* __restrict__ cand_e, int32_t* ids_out,
+                                float* w_out) {
+  const int q = (E + 3) / 4;
+  int base = 0, ncand = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int nw = max(0, min(q, E - w * q));
+    if (w < wave) base += min(k, nw);
+    ncand += min(k, nw);
+  }
+  const int nw = max(0, min(q, E - wave * q)), kw = min(k, nw);
+  if (kw > 0) {
+    float sv[8];
+    int se[8];
+    wave_topk_select_any(row + wave * q, nw, kw, lane, sv, se);
+    if (lane < kw) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j == lane) {
+          cand_v[base + j] = sv[j];
+          cand_e[base + j] = wave * q + se[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float sv[8];
+    int se[8];
+    wave_topk_select<1>(cand_v, ncand, k, lane, sv, se);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) se[j] = cand_e[se[j]];
+    topk_softmax_write(sv, se, k, lane, ids_out, w_out);
+  }
 }
 
 // Exclusive prefix sum over a block of up to 1024 threads (all threads must

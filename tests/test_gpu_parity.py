@@ -121,6 +121,29 @@ def test_topk_non_finite_logits():
     assert np.array_equal(got, oracle.topk_select(lg.numpy().astype(np.float64), k))
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_layer_decode_router_ties(T):
+    """Exactly tied logits spread over the expert range (the single-token top-k
+    splits the experts into quarters and merges): ties go to the lower index."""
+    print("router ties", T, flush=True)
+    H, I, E, k = 256, 128, 256, 6
+    layer = synth.make_layer(1, H, I, E, k, 11, DEV)
+    wr = torch.zeros((E, H), dtype=torch.float32)
+    for e in (250,):
+        wr[e, 0] = 2.0
+    for e in (200, 130, 70, 5):
+        wr[e, 0] = 1.0
+    layer["w_router"] = wr.to(DEV)
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    x[:, 0] = 1.0
+    y, ids, w = run_layer(layer, x, None, T)
+    assert ids.cpu().numpy().tolist() == [[250, 5, 70, 130, 200, 0]] * T
+    layer["w_router"] = torch.zeros((E, H), dtype=torch.float32, device=DEV)
+    y, ids, w = run_layer(layer, x, None, T)
+    assert ids.cpu().numpy().tolist() == [list(range(k))] * T
+    assert np.allclose(w.cpu().numpy(), 1.0 / k)
+
+
 def test_layer_decode_non_finite_tokens():
     """Tokens holding inf / NaN must not disturb the finite tokens of the batch,
     and their expert ids stay valid (regression: an all-NaN logit row once

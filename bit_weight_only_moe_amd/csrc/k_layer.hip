@@ -322,9 +322,14 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   int* scan_tmp = (int*)(off + E + 1);                                  // [17]
   float* cand_v = (float*)(scan_tmp + 17);                              // [4 * 8]
   int32_t* cand_e = (int32_t*)(cand_v + 32);                            // [4 * 8]
+  uint64_t* rk = (uint64_t*)(((uintptr_t)(cand_e + 32) + 15) & ~(uintptr_t)15);  // [kRankScratch]
   copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
   __syncthreads();
-  if (nt == 1)  // a lone token: all four waves share its selection
+  // a lone token: all four waves share its selection (rank counting for up
+  // to 256 experts); several tokens: one per wave
+  if (nt == 1 && E <= 256)
+    block_topk_rank(s_log, E, k, rk, s_ids + t0 * k, s_w + t0 * k);
+  else if (nt == 1)
     block_topk_softmax(s_log, E, k, wave, lane, cand_v, cand_e, s_ids + t0 * k, s_w + t0 * k);
   else if (wave < nt)
     wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
@@ -613,7 +618,7 @@ static DecodeLds decode_lds(int T, int H, int I, int Is, int E, int k) {
   if (T < 1 || T > 64 || E > 1024 || H > 4096) return d;
   const int NT = layer_nt(T);
   const size_t tables =
-      (size_t)T * k * 8 + (size_t)kRouteT * E * 4 + 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 17 * 4 + 64 * 4;
+      (size_t)T * k * 8 + (size_t)kRouteT * E * 4 + 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 17 * 4 + 64 * 4 + 16 + kRankScratch * 8;
   const size_t route = std::max((size_t)router_tokens(T) * H * 2, std::max(tables, stage_bytes(NT, H)));
   const size_t gateup = stage_bytes(NT, H);
   const size_t down = align16(stage_bytes(NT, std::max(I, Is))) + (size_t)T * k * 8;

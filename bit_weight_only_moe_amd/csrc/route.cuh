@@ -262,6 +262,88 @@ MOE_DEV void block_topk_softmax(const float* __restrict__ row, int E, int k, int
   }
 }
 
+// ---- top-k by rank counting (E <= 256) -------------------------------------
+// Latency-bound variant for the routing tails, where one block routes a few
+// tokens while the rest of the chip waits.  Every entry gets a unique 64-bit
+// key whose unsigned order is the selection order above: the order-
+// preserving bits of the value (NaN mapped below every number, -0 folded
+// onto +0) over the complemented index, so equal values rank by lower index.
+// An entry's rank is the number of larger keys, counted with fully unrolled
+// compares against keys read 16 bytes at a time (no serial maximum rounds,
+// no loop branches).  Stage 1 ranks within 64-entry chunks and keeps each
+// chunk's top k; stage 2 ranks those <= 32 candidates.  The selected values
+// and the softmax are those of the round-based selection, bit for bit
+// (a NaN-only pick has the value -inf there, and here).
+constexpr int kRankScratch = 296;  // u64 LDS words: 256 keys, 32 candidates, 8 winners
+
+MOE_DEV uint64_t topk_key(float v, int idx) {
+  const uint32_t hi = (v == v) ? f32_order_key(v) : 0u;
+  return ((uint64_t)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+MOE_DEV float topk_key_value(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  return hi == 0u ? -INFINITY : f32_from_order_key(hi);
+}
+MOE_DEV int topk_key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+// Number of the N keys at K (LDS, 16-byte aligned) larger than `mine`.
+template <int N>
+MOE_DEV int key_rank(const uint64_t* K, uint64_t mine) {
+  const uint4* K4 = (const uint4*)K;
+  int r0 = 0, r1 = 0;
+#pragma unroll
+  for (int b = 0; b < N / 2; b += 8) {
+    uint4 q0 = K4[b], q1 = K4[b + 1], q2 = K4[b + 2], q3 = K4[b + 3];
+    uint4 q4 = K4[b + 4], q5 = K4[b + 5], q6 = K4[b + 6], q7 = K4[b + 7];
+#define MOE_RANK_PAIR(q)                                                          \
+  r0 += (((uint64_t)q.y << 32) | q.x) > mine;                                    \
+  r1 += (((uint64_t)q.w << 32) | q.z) > mine;
+    MOE_RANK_PAIR(q0) MOE_RANK_PAIR(q1) MOE_RANK_PAIR(q2) MOE_RANK_PAIR(q3)
+    MOE_RANK_PAIR(q4) MOE_RANK_PAIR(q5) MOE_RANK_PAIR(q6) MOE_RANK_PAIR(q7)
+#undef MOE_RANK_PAIR
+  }
+  return r0 + r1;
+}
+
+// Stage 2 + softmax for one token, by one wave: C[0..32) holds the stage-1
+// candidates (unused slots 0); F: 8 LDS words.  Lanes j < k write ids_out[j]
+// and w_out[j] = exp(v_j - v_0) / sum_i exp(v_i - v_0), summed in rank order.
+MOE_DEV void rank_finish(const uint64_t* C, uint64_t* F, int k, int lane, int32_t* ids_out, float* w_out) {
+  const uint64_t c = lane < 32 ? C[lane] : 0ull;
+  const int r = key_rank<32>(C, c);
+  if (c != 0ull && r < k) F[r] = c;
+  wave_lds_sync();
+  const uint64_t f = F[lane < k ? lane : 0];
+  const float v0 = topk_key_value(F[0]);
+  const float ex = expf(topk_key_value(f) - v0);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+  if (lane < k) {
+    ids_out[lane] = topk_key_index(f);
+    w_out[lane] = ex / sum;
+  }
+}
+
+// One token (E <= 256) by the 4 waves of a block; thread i owns entry i.
+// S: kRankScratch LDS words.  Call from all 256 threads; two __syncthreads.
+MOE_DEV void block_topk_rank(const float* __restrict__ row, int E, int k, uint64_t* S, int32_t* ids_out,
+                             float* w_out) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint64_t* K = S;
+  uint64_t* C = S + 256;
+  uint64_t* F = S + 288;
+  const uint64_t mine = tid < E ? topk_key(row[tid], tid) : 0ull;
+  K[tid] = mine;
+  if (tid < 32) C[tid] = 0ull;
+  __syncthreads();
+  const int r = key_rank<64>(K + wave * 64, mine);
+  if (tid < E && r < k) C[wave * k + r] = mine;
+  __syncthreads();
+  if (wave == 0) rank_finish(C, F, k, lane, ids_out, w_out);
+}
+
 // Exclusive prefix sum over a block of up to 1024 threads (all threads must
 // call).  `lds` holds at least 17 ints.  Returns this thread's prefix and
 // the block total in `total`.

@@ -30,6 +30,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per measured unit (one layer call; the prefill's grouped FFN) from two rocprofv3
+# --pmc runs of the same workload with the current kernels: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
+# the factors that make the counters read 1 GiB each for a plain 1 GiB device copy
+# (profiles/hbm_traffic_counters.md).  Workloads not listed report null.
+TRAFFIC_BYTES = {
+    ("decode_b1", "nvfp4"): 22.00e6,
+    ("decode_T16", "nvfp4"): 223.8e6,
+    ("prefill", "nvfp4"): 1386.5e6,
+}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -177,8 +187,10 @@ def main():
                    "expert_bytes_per_step": bytes_per_step, "router_bytes_per_step": router_bytes,
                    "distinct_experts_per_step": float(np.mean(touched))},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "moe_layer_decode (whole layer call)"},
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get((workload, args.fmt)),
+                     "kernel": "moe_layer_decode: k_layer_route_shared + k_layer_gateup + k_layer_down_combine "
+                               "(one layer call, events on the launch stream)",
+                     "bytes": "expert weights of the distinct touched experts + shared expert, per call"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
@@ -309,7 +321,8 @@ def bench_prefill(args, fmt):
                    "max_rows_per_expert": int(c.max()), "min_rows_per_expert": int(c.min()), "weight_copies": R},
         "roofline": {"bound": "mfma", "achieved": flops / (ms_ffn / K * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ms_ffn / K * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "kernel": "moe_grouped_w4a16_ffn (routed + shared, MFMA)"},
+                     "traffic": TRAFFIC_BYTES.get(("prefill", args.fmt)),
+                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, k_mfma_gateup, k_mfma_down"},
         "cpu_baseline": None,
     }
     print(json.dumps(out_line))

@@ -62,6 +62,7 @@ hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* cod
 // Block: 4 waves = 4 experts; up to kRouteTok tokens staged in LDS as bf16
 // (at most 64 KB).
 constexpr int kRouteTok = 16;
+constexpr int kRouterMfmaMinT = 256;
 
 __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                        int T, int H, int E, int tpb, float* __restrict__ logits) {
@@ -84,6 +85,8 @@ __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restric
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                                 hipStream_t s) {
+  // large batches: the matrix-core router (decode-sized batches keep the fused path's reduction order)
+  if (T >= kRouterMfmaMinT) return launch_router_mfma(x, wr, T, H, E, logits, s);
   const int tpb = std::max(1, std::min(kRouteTok, 32768 / H));  // <= 64 KB of LDS
   dim3 grid((E + 3) / 4, (T + tpb - 1) / tpb);
   const size_t lds = (size_t)tpb * H * sizeof(uint16_t);

@@ -405,6 +405,136 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
   }
 }
 
+// ------------------------------------------------------------------ router (large batches)
+// logits[t, e] = sum_h x[t, h] * w[e, h] on the matrix cores.  Each fp32
+// router weight is split exactly into three bf16 parts, w = hi + mid + lo
+// (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid, each residual exact
+// in fp32 and the last one exact in bf16), so every product x * part is exact
+// in fp32 and the three MFMAs accumulate them in fp32, as the VALU router's
+// fused multiply-adds do (in another order).  Block: 64 tokens x 64 experts,
+// 4 waves as 2 x 2 of 32 x 32; 64-wide K steps staged through LDS, global
+// data loaded two steps ahead.
+// Named, interleaved fields: adjacent copies from adjacent global addresses
+// are merged into one block copy that the compiler keeps in private memory.
+struct RouterStage {
+  uint4 a0;     // bf16 0..7 of one token row's 16
+  float4 w0;    // fp32 0..3 of one router row's 16
+  uint4 a1;     // bf16 8..15
+  float4 w1, w2, w3;
+};
+
+MOE_DEV void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const __bf16 h = (__bf16)w;
+  const float r1 = w - (float)h;
+  const __bf16 m = (__bf16)r1;
+  const __bf16 l = (__bf16)(r1 - (float)m);
+  hi = __builtin_bit_cast(uint16_t, h);
+  mid = __builtin_bit_cast(uint16_t, m);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// Split two fp32 values into packed bf16 pairs of their hi / mid / lo parts.
+MOE_DEV void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  uint32_t ha, ma, la, hb, mb, lb;
+  split3(a, ha, ma, la);
+  split3(b, hb, mb, lb);
+  hi = ha | (hb << 16);
+  mid = ma | (mb << 16);
+  lo = la | (lb << 16);
+}
+
+// Split 8 fp32 weights into three uint4 of 8 bf16 each.
+MOE_DEV void split3_x8(float4 p, float4 q, uint4& hi, uint4& mid, uint4& lo) {
+  split3_pair(p.x, p.y, hi.x, mid.x, lo.x);
+  split3_pair(p.z, p.w, hi.y, mid.y, lo.y);
+  split3_pair(q.x, q.y, hi.z, mid.z, lo.z);
+  split3_pair(q.z, q.w, hi.w, mid.w, lo.w);
+}
+
+MOE_DEV void router_load(const uint16_t* xrow, const float* wrow, int kt, RouterStage& st) {
+  const uint4* xa = (const uint4*)(xrow + kt * 64);
+  const float4* wa = (const float4*)(wrow + kt * 64);
+  st.a0 = xa[0];
+  st.w0 = wa[0];
+  st.a1 = xa[1];
+  st.w1 = wa[1];
+  st.w2 = wa[2];
+  st.w3 = wa[3];
+}
+
+// Write one K step's token chunk and split router chunks into the tiles.
+MOE_DEV void router_stage(const RouterStage& st, int lrow, int lq, uint4* As, uint4 (*Bs)[64 * 8]) {
+  __syncthreads();
+  As[swz(lrow, lq * 2)] = st.a0;
+  As[swz(lrow, lq * 2 + 1)] = st.a1;
+  uint4 h, m, l;
+  split3_x8(st.w0, st.w1, h, m, l);  // two chunks of 8 weights
+  Bs[0][swz(lrow, lq * 2)] = h;
+  Bs[1][swz(lrow, lq * 2)] = m;
+  Bs[2][swz(lrow, lq * 2)] = l;
+  split3_x8(st.w2, st.w3, h, m, l);
+  Bs[0][swz(lrow, lq * 2 + 1)] = h;
+  Bs[1][swz(lrow, lq * 2 + 1)] = m;
+  Bs[2][swz(lrow, lq * 2 + 1)] = l;
+  __syncthreads();
+}
+
+MOE_DEV void router_compute(const uint4* As, const uint4 (*Bs)[64 * 8], int wm, int wn, int lane, f32x16_t& acc) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int chunk = ks * 2 + (lane >> 5);
+    const bf16x8_t a = lds_frag(As, wm * 32 + (lane & 31), chunk);
+    const int brow = wn * 32 + (lane & 31);
+    acc = mfma(a, lds_frag(Bs[2], brow, chunk), acc);
+    acc = mfma(a, lds_frag(Bs[1], brow, chunk), acc);
+    acc = mfma(a, lds_frag(Bs[0], brow, chunk), acc);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_router_mfma(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                     int T, int H, int E, float* __restrict__ logits) {
+  __shared__ uint4 As[64 * 8];      // [64 tokens][64 k] bf16, swizzled
+  __shared__ uint4 Bs[3][64 * 8];   // hi / mid / lo parts of [64 experts][64 k]
+  const int nte = (E + 63) / 64;
+  const int t0 = (blockIdx.x / nte) * 64, e0 = (blockIdx.x % nte) * 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  // loaders: token row tid >> 2, 16 bf16 at (tid & 3) * 16; router row tid >> 2, 16 fp32 at (tid & 3) * 16
+  const int lrow = tid >> 2, lq = tid & 3;
+  const uint16_t* xrow = x + (size_t)min(t0 + lrow, T - 1) * H + lq * 16;
+  const float* wrow = wr + (size_t)min(e0 + lrow, E - 1) * H + lq * 16;
+  f32x16_t acc = f32x16_t{};
+  const int nk = H / 64;
+  RouterStage s0, s1;
+  router_load(xrow, wrow, 0, s0);
+  if (nk > 1) router_load(xrow, wrow, 1, s1);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    router_stage(s0, lrow, lq, As, Bs);
+    if (kt + 2 < nk) router_load(xrow, wrow, kt + 2, s0);
+    router_compute(As, Bs, wm, wn, lane, acc);
+    router_stage(s1, lrow, lq, As, Bs);
+    if (kt + 3 < nk) router_load(xrow, wrow, kt + 3, s1);
+    router_compute(As, Bs, wm, wn, lane, acc);
+  }
+  if (kt < nk) {
+    router_stage(s0, lrow, lq, As, Bs);
+    router_compute(As, Bs, wm, wn, lane, acc);
+  }
+  const int col = e0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = t0 + wm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+    if (row < T && col < E) logits[(size_t)row * E + col] = acc[i];
+  }
+}
+
+hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, int E, float* logits, hipStream_t s) {
+  const unsigned blocks = (unsigned)(((T + 63) / 64) * ((E + 63) / 64));
+  hipLaunchKernelGGL(k_router_mfma, dim3(blocks), dim3(256), 0, s, x, wr, T, H, E, logits);
+  return hipGetLastError();
+}
+
 size_t mfma_ws_bytes(int E, int H, int I, int total_rows) {
   const size_t max_tiles = (size_t)total_rows / kBM + E + 1;
   const size_t t = (1 + 2 * max_tiles) * sizeof(int32_t);

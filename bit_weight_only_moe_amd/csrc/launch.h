@@ -13,6 +13,9 @@ namespace moe {
 
 hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* codes, const void* scales,
                                  const uint8_t* zeros, const float* ts_dev, float* out, hipStream_t s);
+// Router logits on the matrix cores (fp32 weights split exactly into three
+// bf16 parts); used for large batches.
+hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, int E, float* logits, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                                 hipStream_t s);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);

@@ -162,11 +162,14 @@ def test_layer_decode_non_finite_tokens():
     check_layer(layer, x, x, y, ids, w, tokens=[0])
 
 
-@pytest.mark.parametrize("T", [1, 5, 64])
-def test_route_logits_and_ids(T):
-    print("route", T, flush=True)
-    H, E, k = 2048, 256, 6
-    layer = synth.make_layer(1, H, 768, E, k, seed=30 + T, device=DEV, shared=False)
+@pytest.mark.parametrize("T,H,E", [(1, 2048, 256), (5, 2048, 256), (64, 2048, 256), (300, 2048, 256),
+                                   (4096, 2048, 256), (300, 192, 100)])
+def test_route_logits_and_ids(T, H, E):
+    """Router logits within 2^-20 sum|x w| of fp64 (T >= 256 runs the matrix-core router with
+    the weights split exactly into three bf16 parts), ids equal to the oracle's off near-ties."""
+    print("route", T, H, E, flush=True)
+    k = 6
+    layer = synth.make_layer(1, H, 128, E, k, seed=30 + T, device=DEV, shared=False)
     x = synth.make_tokens(T, H, 30 + T, DEV)
     lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
     ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
@@ -183,7 +186,7 @@ def test_route_logits_and_ids(T):
     assert np.array_equal(oracle.topk_select(lg.cpu().numpy().astype(np.float64), k), gids)
     ties = near_tie_tokens(xb, wr, k)
     assert np.array_equal(gids[~ties], ref_ids[~ties])
-    assert ties.sum() <= 1
+    assert ties.sum() <= max(1, T // 500)
 
 
 # ------------------------------------------------------------------ permute

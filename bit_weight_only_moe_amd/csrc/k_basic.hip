@@ -123,40 +123,38 @@ __global__ void __launch_bounds__(256) k_perm_hist(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block (1024 threads): per-expert totals, exclusive scan, per-chunk bases.
+// One block (1024 threads): per-expert totals and offsets; each histogram
+// entry becomes the exclusive count of earlier chunks for its expert.
 __global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t* __restrict__ hist,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[1024];
-  __shared__ int32_t scan[1025];
+  __shared__ int scan_tmp[17];
   const int e = threadIdx.x;
+  // per expert: exclusive prefix over the chunks (8 loads in flight), written back in place
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;  // exclusive within the expert
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nchunks ? hist[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunks) hist[(size_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
   }
-  tot[e] = (e < E) ? run : 0;
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      scan[i] = acc;
-      acc += tot[i];
-    }
-    scan[E] = acc;
-  }
-  __syncthreads();
+  // experts' totals -> offsets (block-wide scan); the scatter adds offsets[e]
+  int total;
+  const int off = block_exclusive_scan(e < E ? run : 0, scan_tmp, total);
   if (e < E) {
-    counts[e] = tot[e];
-    offsets[e] = scan[e];
-    for (int c = 0; c < nchunks; ++c) hist[(size_t)c * E + e] += scan[e];
+    counts[e] = run;
+    offsets[e] = off;
   }
-  if (e == 0) offsets[E] = scan[E];
+  if (e == 0) offsets[E] = total;
 }
 
 __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,
+                                                      const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ base,
                                                       int32_t* __restrict__ sorted_pairs,
                                                       int32_t* __restrict__ pair_pos) {
@@ -170,7 +168,7 @@ __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict_
   const int e = cid[i];
   int rank = 0;
   for (int q = 0; q < i; ++q) rank += (cid[q] == e);
-  const int pos = base[(size_t)blockIdx.x * E + e] + rank;
+  const int pos = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
   sorted_pairs[pos] = p;
   pair_pos[p] = pos;
 }
@@ -200,7 +198,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   int32_t* hist = (int32_t*)ws;
   hipLaunchKernelGGL(k_perm_hist, dim3(nchunks), dim3(kPermChunk), E * sizeof(int32_t), s, ids, n, E, hist);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, nchunks, E, hist, counts, offsets);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, hist, sorted_pairs, pair_pos);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, offsets, hist, sorted_pairs,
+                     pair_pos);
   if (x && x_perm) hipLaunchKernelGGL(k_gather_rows, dim3(n), dim3(256), 0, s, x, sorted_pairs, k, H, x_perm);
   return hipGetLastError();
 }

@@ -6,9 +6,13 @@
 // Per expert e with rows [offsets[e], offsets[e+1]) (tokens gathered through
 // sorted_pairs):
 //   gate/up kernel: G = X_e Wg_e^T, U = X_e Wu_e^T over K = H, then
-//                   h = bf16(silu(G) * U) for a 128-row x 64-feature tile;
-//   down kernel:    O = h_e Wd_e^T over K = I, fp32, 128 x 128 tiles.
-// A device-side tile table lists (expert, first row) for every 128-row tile.
+//                   h = bf16(silu(G) * U);
+//   down kernel:    O = h_e Wd_e^T over K = I, fp32.
+// A device-side table lists (expert, first row) for every 128-row tile.
+// When the shapes allow, an expert's final remainder of at most 64 rows goes
+// to a second table of 64-row tiles (4 waves side by side instead of 2 x 2):
+// with Zipf-skewed routing most experts get a few dozen rows, and a 128-row
+// tile would spend half of its matrix work and LDS traffic on padding.
 //
 // Weights are dequantised once per 64-wide K step into LDS as bf16:
 //   NVFP4: e4m3 * e2m1 has at most 6 significant bits, so the bf16 operand is
@@ -18,12 +22,12 @@
 //          scale in fp32 (s * (q - z) itself would not be exact in bf16).
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operands: lane l supplies row (A) or column
 // (B) l % 32 and 8 consecutive k values; the accumulator register i of lane l
-// holds row (i / 4) * 8 + (l / 32) * 4 + i % 4, column l % 32.
-// LDS tiles are [128 rows][64 k] bf16 with the 16-byte chunk index XOR-ed by
+// holds row (i / 4) * 8 + (l / 32) * 4 + i % 4, column l % 32.  Each wave
+// owns a 64 x 64 output tile (2 x 2 accumulators).
+// LDS tiles are [rows][64 k] bf16 with the 16-byte chunk index XOR-ed by
 // row & 7: a 128-byte row spans all 32 banks, so the 8 lanes that one LDS
 // cycle serves for a 16-byte access (8 consecutive rows at one chunk, or 4
-// rows at chunks c and c + 4) land on distinct banks.  Two tile buffers
-// alternate between K steps, so each step needs one barrier.
+// rows at chunks c and c + 4) land on distinct banks.
 #include "common.cuh"
 #include "launch.h"
 #include "route.cuh"
@@ -33,7 +37,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;  // rows (tokens) per tile
+constexpr int kBM = 128;  // rows per full tile; remainders of <= 64 rows may use 64-row tiles
 constexpr int kBK = 64;   // reduction step = one INT4 group
 
 struct MfmaArgs {
@@ -42,6 +46,7 @@ struct MfmaArgs {
   const int32_t* sorted_pairs;  // NULL: sorted row r is token r
   const int32_t* offsets;       // [E + 1]; NULL: one expert over rows [0, rows)
   const int32_t* tiles;         // [0] = count, then (expert, first row) pairs
+  int tile_rows;                // rows per tile of that table: 128 or 64
   const uint8_t *gc, *gs, *gz;  // gate codes / scales / zeros
   const uint8_t *uc, *us, *uz;  // up
   const uint8_t *dc, *ds, *dz;  // down
@@ -101,13 +106,15 @@ MOE_DEV bool tile_of(const MfmaArgs& g, int mt, int& e, int& r0, int& r1) {
   e = g.tiles[1 + 2 * mt];
   r0 = g.tiles[2 + 2 * mt];
   const int end = g.offsets ? g.offsets[e + 1] : g.rows;
-  r1 = min(end, r0 + kBM);
+  r1 = min(end, r0 + g.tile_rows);
   return true;
 }
 
-// Tile table: one block; expert e contributes ceil(count_e / 128) tiles.
-__global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__ offsets, int E, int rows,
-                                                     int32_t* __restrict__ tiles) {
+// Tile tables, one block: each expert's rows in 128-row tiles (`big`); with
+// `split`, a final remainder of 1..64 rows becomes one 64-row tile (`small`)
+// instead.  Each table: [0] = count, then (expert, first row) pairs.
+__global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__ offsets, int E, int rows, int split,
+                                                     int32_t* __restrict__ big, int32_t* __restrict__ small) {
   __shared__ int scan_lds[17];
   const int e = threadIdx.x;
   int r0 = 0, r1 = 0;
@@ -115,26 +122,40 @@ __global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__
     r0 = offsets ? offsets[e] : 0;
     r1 = offsets ? offsets[e + 1] : rows;
   }
-  const int nt = (r1 - r0 + kBM - 1) / kBM;
-  int total;
-  const int first = block_exclusive_scan(nt, scan_lds, total);
-  for (int t = 0; t < nt; ++t) {
-    tiles[1 + 2 * (first + t)] = e;
-    tiles[2 + 2 * (first + t)] = r0 + t * kBM;
+  const int c = r1 - r0, rem = c % kBM;
+  const bool to_small = split && rem > 0 && rem <= 64;
+  const int nb = c / kBM + ((rem > 0 && !to_small) ? 1 : 0);
+  const int ns = to_small ? 1 : 0;
+  int tb, ts;
+  const int fb = block_exclusive_scan(nb, scan_lds, tb);
+  const int fs = block_exclusive_scan(ns, scan_lds, ts);
+  for (int t = 0; t < nb; ++t) {
+    big[1 + 2 * (fb + t)] = e;
+    big[2 + 2 * (fb + t)] = r0 + t * kBM;
   }
-  if (e == 0) tiles[0] = total;
+  if (ns) {
+    small[1 + 2 * fs] = e;
+    small[2 + 2 * fs] = r0 + (c / kBM) * kBM;
+  }
+  if (e == 0) {
+    big[0] = tb;
+    small[0] = ts;
+  }
 }
 
-// One K step's global data for this thread, loaded two steps ahead of its
-// use (two register sets in turn) so that the memory latency is covered by
-// the matrix work of the steps in between.
-struct MfmaStage {
-  uint4 a[4];      // 4 x 8 bf16 of one activation row
-  uint4 b;         // 32 packed 4-bit weights of one weight row
-  uint32_t sc;     // NVFP4: the two e4m3 block scales of those 32 weights
-  int z;           // INT4: zero point of this K step's group
-  float s0, s1;    // INT4: this wave's two per-column group scales (fp16 -> fp32)
-};
+// One K step's global data for this thread is loaded two steps ahead of its
+// use, into two sets of plain registers in turn (a struct or array here is
+// copied through private memory by the compiler), so the memory latency is
+// covered by the matrix work of the steps in between.  A set: activation
+// chunks a0..a3 (2 x 2 waves: 4 per thread; 4 x 1: a0, a1), weight codes b0
+// (4 x 1: and b1, the row's next 32 weights), NVFP4 block scales sc, INT4
+// zero point z and this wave's two per-column group scales s0, s1.
+#define MOE_STAGE_VARS(p) \
+  uint4 p##a0, p##a1, p##a2, p##a3, p##b0, p##b1; \
+  uint32_t p##sc = 0; \
+  int p##z = 0; \
+  float p##s0 = 1.f, p##s1 = 1.f
+#define MOE_STAGE_ARGS(p) p##a0, p##a1, p##a2, p##a3, p##b0, p##b1, p##sc, p##z, p##s0, p##s1
 
 // Map the block index to (row tile, column slice) so that every column slice
 // of a row tile runs on the same XCD (blocks go to XCDs round-robin), and the
@@ -145,30 +166,85 @@ MOE_DEV void block_tile(int nslices, int& tile, int& slice) {
   slice = j % nslices;
 }
 
+// Write one K step's activation chunks and dequantised weights into the
+// (single) LDS tiles, between two barriers.  WM = 2: thread = (row tid >> 1,
+// chunks (tid & 1) * 4 .. + 4) for A and (row (tid >> 1) & 63 of matrix
+// tid >> 7, half tid & 1) for B.  WM = 1: (row tid >> 2, chunks (tid & 3) * 2
+// .. + 2) for A and (row tid & 127 of matrix tid >> 7, both halves) for B.
+template <int FMT, int WM>
+MOE_DEV void mfma_step(uint4 a0, uint4 a1, uint4 a2, uint4 a3, uint4 b0, uint4 b1, uint32_t sc, int z, uint4* As,
+                       uint4* Bs, int a_row, int a_c0, int b_lrow, int b_half) {
+  __syncthreads();
+  As[swz(a_row, a_c0)] = a0;
+  As[swz(a_row, a_c0 + 1)] = a1;
+  if (WM == 2) {
+    As[swz(a_row, a_c0 + 2)] = a2;
+    As[swz(a_row, a_c0 + 3)] = a3;
+  }
+  uint4 o[4];
+  dequant32<FMT>(b0, sc, z, o);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) Bs[swz(b_lrow, b_half * 4 + c)] = o[c];
+  if (WM == 1) {
+    dequant32<FMT>(b1, sc >> 16, z, o);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Bs[swz(b_lrow, 4 + c)] = o[c];
+  }
+  __syncthreads();
+}
+
+// Load K step kt's data for this thread (see MOE_STAGE_VARS).
+template <int FMT, int WM>
+MOE_DEV void mfma_load(int kt, const uint16_t* arow, int a_c0, const uint8_t* bcodes, const uint8_t* bscales,
+                       const uint8_t* bzeros_row, const uint16_t* sc0, const uint16_t* sc1, uint4& a0, uint4& a1,
+                       uint4& a2, uint4& a3, uint4& b0, uint4& b1, uint32_t& sc, int& z, float& s0, float& s1) {
+  const uint4* xa = (const uint4*)(arow + kt * kBK) + a_c0;
+  const uint4* wb = (const uint4*)(bcodes + kt * (kBK / 2));
+  a0 = xa[0];
+  b0 = wb[0];
+  a1 = xa[1];
+  if (WM == 2) {
+    a2 = xa[2];
+    a3 = xa[3];
+  } else {
+    b1 = wb[1];
+  }
+  if (FMT == kFmtNvfp4) {
+    sc = WM == 2 ? *(const uint16_t*)(bscales + kt * 4) : *(const uint32_t*)(bscales + kt * 4);
+  } else {
+    z = bzeros_row[kt];
+    s0 = f16_to_f32(sc0[kt]);
+    s1 = f16_to_f32(sc1[kt]);
+  }
+}
+
 // ------------------------------------------------------------------ gate/up
-// Block: 4 waves as 2 (rows) x 2 (features); each wave owns a 64-row x 32-
-// feature tile of both G and U (2 x 2 accumulators of 32 x 32).
-template <int FMT>
+// Block: 4 waves as WM (rows) x WN = 4 / WM (features); each wave owns a
+// 64-row x 32-feature tile of both G and U.  The block covers 64 * WM rows and
+// 32 * WN features of gate and of up.
+template <int FMT, int WM>
 __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
-  __shared__ uint4 As2[2][kBM * 8];  // [128][64] bf16, swizzled
-  __shared__ uint4 Bs2[2][128 * 8];  // rows 0..63 gate, 64..127 up
+  constexpr int WN = 4 / WM, BMr = 64 * WM, NF = 32 * WN;
+  __shared__ uint4 As[BMr * 8];     // [BMr][64] bf16, swizzled
+  __shared__ uint4 Bs[2 * NF * 8];  // rows 0..NF-1 gate, NF..2NF-1 up
   int tile, slice;
-  block_tile(g.I / 64, tile, slice);
+  block_tile(g.I / NF, tile, slice);
   int e, r0, r1;
   if (!tile_of(g, tile, e, r0, r1)) return;
   const int H = g.H, I = g.I;
-  const int n0 = slice * 64;
+  const int n0 = slice * NF;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  // loader roles: A row tid >> 1, 4 chunks from (tid & 1) * 4; B matrix tid >> 7, row (tid >> 1) & 63, half tid & 1
-  const int a_row = tid >> 1, a_c0 = (tid & 1) * 4;
-  const bool a_valid = r0 + a_row < r1;
-  const int tok = a_valid ? (g.sorted_pairs ? g.sorted_pairs[r0 + a_row] / g.k : r0 + a_row) : 0;
+  const int wm = wave / WN, wn = wave % WN;
+  const int a_row = WM == 2 ? tid >> 1 : tid >> 2, a_c0 = WM == 2 ? (tid & 1) * 4 : (tid & 3) * 2;
+  // rows past the tile's end load a valid row; their outputs are never stored
+  const int arow = min(r0 + a_row, r1 - 1);
+  const int tok = g.sorted_pairs ? g.sorted_pairs[arow] / g.k : arow;
   const uint16_t* xrow = g.x + (size_t)tok * H;
-  const int b_mat = tid >> 7, b_row = (tid >> 1) & 63, b_half = tid & 1;
+  const int b_mat = tid >> 7, b_row = WM == 2 ? (tid >> 1) & 63 : tid & 127, b_half = WM == 2 ? tid & 1 : 0;
+  const int b_lrow = b_mat * NF + b_row;
   const size_t wrow = (size_t)e * I + n0 + b_row;
   const uint8_t* bcodes = (b_mat ? g.uc : g.gc) + wrow * (H / 2) + b_half * 16;
-  const uint8_t* bscales = b_mat ? g.us : g.gs;
+  const uint8_t* bscales = (b_mat ? g.us : g.gs) + wrow * (H / 16) + b_half * 2;
   const uint8_t* bzeros = b_mat ? g.uz : g.gz;
   // this wave's gate / up feature column (INT4 group scales)
   const int ncol = n0 + wn * 32 + (lane & 31);
@@ -182,62 +258,33 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
     for (int m = 0; m < 2; ++m) acc[a][m] = f32x16_t{};
 
   const int nk = H / kBK;
-  auto load = [&](int kt, MfmaStage& st) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st.a[c] = a_valid ? ((const uint4*)(xrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
-    st.b = *(const uint4*)(bcodes + kt * (kBK / 2));
-    if (FMT == kFmtNvfp4) {
-      st.sc = *(const uint16_t*)(bscales + wrow * (H / 16) + kt * 4 + b_half * 2);
-    } else {
-      st.z = bzeros[wrow * (H / 64) + kt];
-      st.s0 = f16_to_f32(gsc[kt]);
-      st.s1 = f16_to_f32(usc[kt]);
-    }
-  };
-  // Write this K step's tiles into buffer `buf`.  The buffer was last read
-  // two steps ago, before every wave passed the previous step's barrier.
-  auto step = [&](const MfmaStage& st, int buf) {
-    uint4* As = As2[buf];
-    uint4* Bs = Bs2[buf];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = st.a[c];
-    {
-      uint4 o[4];
-      dequant32<FMT>(st.b, st.sc, st.z, o);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) Bs[swz(b_mat * 64 + b_row, b_half * 4 + c)] = o[c];
-    }
-    __syncthreads();
-  };
+  const uint8_t* bzrow = bzeros ? bzeros + wrow * (H / 64) : nullptr;
   // NVFP4 accumulates straight into acc; INT4 accumulates one group in part
   // and adds it to acc times the group's scale.
-  auto mma = [&](f32x16_t (&c)[2][2], int buf) {
-    const uint4* As = As2[buf];
-    const uint4* Bs = Bs2[buf];
+  auto mma = [&](f32x16_t (&c)[2][2]) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
       const bf16x8_t a0 = lds_frag(As, wm * 64 + (lane & 31), chunk);
       const bf16x8_t a1 = lds_frag(As, wm * 64 + 32 + (lane & 31), chunk);
       const bf16x8_t bg = lds_frag(Bs, wn * 32 + (lane & 31), chunk);
-      const bf16x8_t bu = lds_frag(Bs, 64 + wn * 32 + (lane & 31), chunk);
+      const bf16x8_t bu = lds_frag(Bs, NF + wn * 32 + (lane & 31), chunk);
       c[0][0] = mfma(a0, bg, c[0][0]);
       c[0][1] = mfma(a1, bg, c[0][1]);
       c[1][0] = mfma(a0, bu, c[1][0]);
       c[1][1] = mfma(a1, bu, c[1][1]);
     }
   };
-  auto compute = [&](float sg, float su, int buf) {
+  auto compute = [&](float sg, float su) {
     if (FMT == kFmtNvfp4) {
-      mma(acc, buf);
+      mma(acc);
     } else {
       f32x16_t part[2][2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int m = 0; m < 2; ++m) part[a][m] = f32x16_t{};
-      mma(part, buf);
+      mma(part);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -248,23 +295,25 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
       }
     }
   };
-  MfmaStage s0, s1;
-  load(0, s0);
-  if (nk > 1) load(1, s1);
+  MOE_STAGE_VARS(p_);
+  MOE_STAGE_VARS(q_);
+  mfma_load<FMT, WM>(0, xrow, a_c0, bcodes, bscales, bzrow, gsc, usc, MOE_STAGE_ARGS(p_));
+  if (nk > 1) mfma_load<FMT, WM>(1, xrow, a_c0, bcodes, bscales, bzrow, gsc, usc, MOE_STAGE_ARGS(q_));
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    step(s0, 0);
-    const float q0 = s0.s0, q1 = s0.s1;
-    if (kt + 2 < nk) load(kt + 2, s0);
-    compute(q0, q1, 0);
-    step(s1, 1);
-    const float p0 = s1.s0, p1 = s1.s1;
-    if (kt + 3 < nk) load(kt + 3, s1);
-    compute(p0, p1, 1);
+    mfma_step<FMT, WM>(p_a0, p_a1, p_a2, p_a3, p_b0, p_b1, p_sc, p_z, As, Bs, a_row, a_c0, b_lrow, b_half);
+    float gs0 = p_s0, gs1 = p_s1;
+    if (kt + 2 < nk) mfma_load<FMT, WM>(kt + 2, xrow, a_c0, bcodes, bscales, bzrow, gsc, usc, MOE_STAGE_ARGS(p_));
+    compute(gs0, gs1);
+    mfma_step<FMT, WM>(q_a0, q_a1, q_a2, q_a3, q_b0, q_b1, q_sc, q_z, As, Bs, a_row, a_c0, b_lrow, b_half);
+    gs0 = q_s0;
+    gs1 = q_s1;
+    if (kt + 3 < nk) mfma_load<FMT, WM>(kt + 3, xrow, a_c0, bcodes, bscales, bzrow, gsc, usc, MOE_STAGE_ARGS(q_));
+    compute(gs0, gs1);
   }
   if (kt < nk) {  // odd number of K steps
-    step(s0, 0);
-    compute(s0.s0, s0.s1, 0);
+    mfma_step<FMT, WM>(p_a0, p_a1, p_a2, p_a3, p_b0, p_b1, p_sc, p_z, As, Bs, a_row, a_c0, b_lrow, b_half);
+    compute(p_s0, p_s1);
   }
   // epilogue: h = bf16(silu(ts_g * G) * (ts_u * U))
   const float tsg = FMT == kFmtNvfp4 ? g.gts[e] : 1.f, tsu = FMT == kFmtNvfp4 ? g.uts[e] : 1.f;
@@ -282,25 +331,27 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
 }
 
 // ------------------------------------------------------------------ down
-// Block: 4 waves as 2 x 2, each a 64-row x 64-column tile (2 x 2 accumulators).
-template <int FMT>
+// Block: 4 waves as WM x WN = 4 / WM, each a 64-row x 64-column tile; the
+// block covers 64 * WM rows and 64 * WN output columns.
+template <int FMT, int WM>
 __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
-  __shared__ uint4 As2[2][kBM * 8];
-  __shared__ uint4 Bs2[2][128 * 8];
+  constexpr int WN = 4 / WM, BMr = 64 * WM, NC = 64 * WN;
+  __shared__ uint4 As[BMr * 8];
+  __shared__ uint4 Bs[NC * 8];
   int tile, slice;
-  block_tile(g.H / 128, tile, slice);
+  block_tile(g.H / NC, tile, slice);
   int e, r0, r1;
   if (!tile_of(g, tile, e, r0, r1)) return;
   const int H = g.H, I = g.I;
-  const int n0 = slice * 128;
+  const int n0 = slice * NC;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int a_row = tid >> 1, a_c0 = (tid & 1) * 4;
-  const bool a_valid = r0 + a_row < r1;
-  const uint16_t* hrow = g.h + (size_t)(a_valid ? r0 + a_row : r0) * I;
-  const int b_row = tid >> 1, b_half = tid & 1;
+  const int wm = wave / WN, wn = wave % WN;
+  const int a_row = WM == 2 ? tid >> 1 : tid >> 2, a_c0 = WM == 2 ? (tid & 1) * 4 : (tid & 3) * 2;
+  const uint16_t* hrow = g.h + (size_t)min(r0 + a_row, r1 - 1) * I;
+  const int b_row = WM == 2 ? tid >> 1 : tid, b_half = WM == 2 ? tid & 1 : 0;
   const size_t wrow = (size_t)e * H + n0 + b_row;
   const uint8_t* bcodes = g.dc + wrow * (I / 2) + b_half * 16;
+  const uint8_t* bscales = g.ds + wrow * (I / 16) + b_half * 2;
   const int ncol0 = n0 + wn * 64 + (lane & 31);
   const uint16_t* dsc0 = (const uint16_t*)g.ds + ((size_t)e * H + ncol0) * (I / 64);
   const uint16_t* dsc1 = (const uint16_t*)g.ds + ((size_t)e * H + ncol0 + 32) * (I / 64);
@@ -311,35 +362,8 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x16_t{};
   const int nk = I / kBK;
-  auto load = [&](int kt, MfmaStage& st) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st.a[c] = a_valid ? ((const uint4*)(hrow + kt * kBK))[a_c0 + c] : make_uint4(0, 0, 0, 0);
-    st.b = *(const uint4*)(bcodes + kt * (kBK / 2));
-    if (FMT == kFmtNvfp4) {
-      st.sc = *(const uint16_t*)(g.ds + wrow * (I / 16) + kt * 4 + b_half * 2);
-    } else {
-      st.z = g.dz[wrow * (I / 64) + kt];
-      st.s0 = f16_to_f32(dsc0[kt]);
-      st.s1 = f16_to_f32(dsc1[kt]);
-    }
-  };
-  auto step = [&](const MfmaStage& st, int buf) {
-    uint4* As = As2[buf];
-    uint4* Bs = Bs2[buf];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) As[swz(a_row, a_c0 + c)] = st.a[c];
-    {
-      uint4 o[4];
-      dequant32<FMT>(st.b, st.sc, st.z, o);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) Bs[swz(b_row, b_half * 4 + c)] = o[c];
-    }
-    __syncthreads();
-  };
-  auto mma = [&](f32x16_t (&c)[2][2], int buf) {
-    const uint4* As = As2[buf];
-    const uint4* Bs = Bs2[buf];
+  const uint8_t* bzrow = g.dz ? g.dz + wrow * (I / 64) : nullptr;
+  auto mma = [&](f32x16_t (&c)[2][2]) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -353,16 +377,16 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
       c[1][1] = mfma(a1, b1, c[1][1]);
     }
   };
-  auto compute = [&](float s0, float s1, int buf) {
+  auto compute = [&](float s0, float s1) {
     if (FMT == kFmtNvfp4) {
-      mma(acc, buf);
+      mma(acc);
     } else {
       f32x16_t part[2][2];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n) part[m][n] = f32x16_t{};
-      mma(part, buf);
+      mma(part);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -373,23 +397,25 @@ __global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
       }
     }
   };
-  MfmaStage s0, s1;
-  load(0, s0);
-  if (nk > 1) load(1, s1);
+  MOE_STAGE_VARS(p_);
+  MOE_STAGE_VARS(q_);
+  mfma_load<FMT, WM>(0, hrow, a_c0, bcodes, bscales, bzrow, dsc0, dsc1, MOE_STAGE_ARGS(p_));
+  if (nk > 1) mfma_load<FMT, WM>(1, hrow, a_c0, bcodes, bscales, bzrow, dsc0, dsc1, MOE_STAGE_ARGS(q_));
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    step(s0, 0);
-    const float q0 = s0.s0, q1 = s0.s1;
-    if (kt + 2 < nk) load(kt + 2, s0);
-    compute(q0, q1, 0);
-    step(s1, 1);
-    const float p0 = s1.s0, p1 = s1.s1;
-    if (kt + 3 < nk) load(kt + 3, s1);
-    compute(p0, p1, 1);
+    mfma_step<FMT, WM>(p_a0, p_a1, p_a2, p_a3, p_b0, p_b1, p_sc, p_z, As, Bs, a_row, a_c0, b_row, b_half);
+    float ds0 = p_s0, ds1 = p_s1;
+    if (kt + 2 < nk) mfma_load<FMT, WM>(kt + 2, hrow, a_c0, bcodes, bscales, bzrow, dsc0, dsc1, MOE_STAGE_ARGS(p_));
+    compute(ds0, ds1);
+    mfma_step<FMT, WM>(q_a0, q_a1, q_a2, q_a3, q_b0, q_b1, q_sc, q_z, As, Bs, a_row, a_c0, b_row, b_half);
+    ds0 = q_s0;
+    ds1 = q_s1;
+    if (kt + 3 < nk) mfma_load<FMT, WM>(kt + 3, hrow, a_c0, bcodes, bscales, bzrow, dsc0, dsc1, MOE_STAGE_ARGS(q_));
+    compute(ds0, ds1);
   }
   if (kt < nk) {  // odd number of K steps
-    step(s0, 0);
-    compute(s0.s0, s0.s1, 0);
+    mfma_step<FMT, WM>(p_a0, p_a1, p_a2, p_a3, p_b0, p_b1, p_sc, p_z, As, Bs, a_row, a_c0, b_row, b_half);
+    compute(p_s0, p_s1);
   }
   const float ts = FMT == kFmtNvfp4 ? g.dts[e] : 1.f;
 #pragma unroll
@@ -535,22 +561,30 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, 
   return hipGetLastError();
 }
 
+static size_t big_tiles_max(int E, int total_rows) { return (size_t)total_rows / kBM + E + 1; }
+static size_t tables_bytes(int E, int total_rows) {
+  const size_t t = (1 + 2 * big_tiles_max(E, total_rows) + 1 + 2 * ((size_t)E + 1)) * sizeof(int32_t);
+  return (t + 255) & ~(size_t)255;
+}
+
 size_t mfma_ws_bytes(int E, int H, int I, int total_rows) {
-  const size_t max_tiles = (size_t)total_rows / kBM + E + 1;
-  const size_t t = (1 + 2 * max_tiles) * sizeof(int32_t);
   (void)H;
-  return ((t + 255) & ~(size_t)255) + (((size_t)total_rows * I * 2 + 255) & ~(size_t)255);
+  return tables_bytes(E, total_rows) + (((size_t)total_rows * I * 2 + 255) & ~(size_t)255);
 }
 
 bool mfma_shape_ok(int H, int I) { return H % 128 == 0 && I % 64 == 0; }
 
+// 64-row remainder tiles need 128-feature gate/up slices and 256-column down slices.
+static bool small_tiles_ok(int H, int I) { return I % 128 == 0 && H % 256 == 0; }
+
 hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* offsets, const int32_t* sorted_pairs,
                                int k, const uint16_t* x, int H, int I, int total_rows, float* out, void* ws,
                                hipStream_t s) {
-  const size_t max_tiles = (size_t)total_rows / kBM + E + 1;
-  int32_t* tiles = (int32_t*)ws;
-  const size_t t = (1 + 2 * max_tiles) * sizeof(int32_t);
-  uint16_t* h = (uint16_t*)((char*)ws + ((t + 255) & ~(size_t)255));
+  const size_t max_big = big_tiles_max(E, total_rows);
+  int32_t* big = (int32_t*)ws;
+  int32_t* small = big + 1 + 2 * max_big;
+  uint16_t* h = (uint16_t*)((char*)ws + tables_bytes(E, total_rows));
+  const bool split = small_tiles_ok(H, I);
   MfmaArgs g;
   g.H = H;
   g.I = I;
@@ -559,7 +593,6 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.x = x;
   g.sorted_pairs = sorted_pairs;
   g.offsets = offsets;
-  g.tiles = tiles;
   g.gc = w->gate.codes;
   g.gs = (const uint8_t*)w->gate.scales;
   g.gz = w->gate.zeros;
@@ -574,16 +607,25 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.dts = w->down.tensor_scale;
   g.h = h;
   g.out = out;
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, tiles);
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, split ? 1 : 0, big, small);
   // one block per (row tile, column slice); tiles rounded up to a multiple of the 8 XCDs
-  const unsigned tiles8 = (unsigned)((max_tiles + 7) / 8 * 8);
-  const dim3 ga(tiles8 * (I / 64)), gd(tiles8 * (H / 128));
-  if (w->gate.fmt == kFmtNvfp4) {
-    hipLaunchKernelGGL(k_mfma_gateup<kFmtNvfp4>, ga, dim3(256), 0, s, g);
-    hipLaunchKernelGGL(k_mfma_down<kFmtNvfp4>, gd, dim3(256), 0, s, g);
+  const unsigned big8 = (unsigned)((max_big + 7) / 8 * 8), small8 = (unsigned)((E + 7) / 8 * 8);
+  MfmaArgs gb = g, gs = g;
+  gb.tiles = big;
+  gb.tile_rows = kBM;
+  gs.tiles = small;
+  gs.tile_rows = 64;
+  const bool nv = w->gate.fmt == kFmtNvfp4;
+  if (nv) {
+    hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
+    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), dim3(small8 * (I / 128)), dim3(256), 0, s, gs);
+    hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
+    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dim3(small8 * (H / 256)), dim3(256), 0, s, gs);
   } else {
-    hipLaunchKernelGGL(k_mfma_gateup<kFmtInt4>, ga, dim3(256), 0, s, g);
-    hipLaunchKernelGGL(k_mfma_down<kFmtInt4>, gd, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
+    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), dim3(small8 * (I / 128)), dim3(256), 0, s, gs);
+    hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
+    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dim3(small8 * (H / 256)), dim3(256), 0, s, gs);
   }
   return hipGetLastError();
 }

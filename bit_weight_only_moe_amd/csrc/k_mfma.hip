@@ -223,7 +223,7 @@ MOE_DEV void mfma_load(int kt, const uint16_t* arow, int a_c0, const uint8_t* bc
 // 64-row x 32-feature tile of both G and U.  The block covers 64 * WM rows and
 // 32 * WN features of gate and of up.
 template <int FMT, int WM>
-__global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
+__global__ void __launch_bounds__(256, 2) k_mfma_gateup(MfmaArgs g) {
   constexpr int WN = 4 / WM, BMr = 64 * WM, NF = 32 * WN;
   __shared__ uint4 As[BMr * 8];     // [BMr][64] bf16, swizzled
   __shared__ uint4 Bs[2 * NF * 8];  // rows 0..NF-1 gate, NF..2NF-1 up
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(256) k_mfma_gateup(MfmaArgs g) {
 // Block: 4 waves as WM x WN = 4 / WM, each a 64-row x 64-column tile; the
 // block covers 64 * WM rows and 64 * WN output columns.
 template <int FMT, int WM>
-__global__ void __launch_bounds__(256) k_mfma_down(MfmaArgs g) {
+__global__ void __launch_bounds__(256, (WM == 1 && FMT == kFmtNvfp4) ? 3 : 2) k_mfma_down(MfmaArgs g) {
   constexpr int WN = 4 / WM, BMr = 64 * WM, NC = 64 * WN;
   __shared__ uint4 As[BMr * 8];
   __shared__ uint4 Bs[NC * 8];

@@ -36,6 +36,9 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+MOE_DEV uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 constexpr int kBM = 128;  // rows per full tile; remainders of <= 64 rows may use 64-row tiles
 constexpr int kBK = 64;   // reduction step = one INT4 group
@@ -431,6 +434,234 @@ __global__ void __launch_bounds__(256, (WM == 1 && FMT == kFmtNvfp4) ? 3 : 2) k_
   }
 }
 
+// ------------------------------------------------------------------ weights straight into registers
+// Block: 4 waves side by side over the columns, each covering all 32 * RF
+// rows of the tile.  Lane l streams the packed codes of its own B column
+// (l % 32) from HBM into registers ahead of their use, dequantises them there
+// and hands them to the matrix core as the B operand: the weights never pass
+// through LDS and need no barrier.  Only the activations, which the 4 waves
+// share, are staged in LDS (two buffers, one barrier per K step).
+// K order inside a 64-wide step (one INT4 group): matrix slice ks takes
+// k = ks*8 .. +8 from lane half 0 and k = 32 + ks*8 .. +8 from lane half 1,
+// so a lane's 32 weights of a step are one contiguous 16-byte run of codes;
+// the activation fragments are read from LDS in the same order.  Both
+// halves of a slice lie in the same INT4 group.
+// NVFP4 loads the codes and block scales of 4 K steps at once (ring of two
+// such groups): the 4 x 32 bytes a row gives in those steps are one 128-byte
+// line, requested together.  INT4 keeps a ring of 4 single steps (its group
+// partial sums leave no registers for more).
+// GU: column pair cf = 0 / 1 is gate / up feature f = n0 + wave*32 + l%32
+//     (the block covers 128 features); h = bf16(silu(G) * U).
+// !GU: columns n0 + wave*64 + cf*32 + l%32 (the block covers 256 outputs).
+constexpr int kBdMaxSteps = 32;  // K <= 2048
+
+// f(kt) for kt = KT .. nk - 1 as compile-time constants, written out.
+template <int KT, int NMAX, class F>
+MOE_DEV void unrolled_steps(int nk, F& f) {
+  if constexpr (KT < NMAX) {
+    if (KT >= nk) return;
+    f(std::integral_constant<int, KT>{});
+    unrolled_steps<KT + 1, NMAX>(nk, f);
+  }
+}
+
+// NVFP4 needs K to be a whole number of 4-step groups.
+static inline bool bd_k_ok(int fmt, int K) {
+  return K <= kBK * kBdMaxSteps && (fmt != kFmtNvfp4 || K % (4 * kBK) == 0);
+}
+
+template <int FMT, int RF, bool GU>
+__global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
+  constexpr bool NV = FMT == kFmtNvfp4;
+  constexpr int BM = 32 * RF, D = 4, NB = GU ? 128 : 256;
+  constexpr int AV = BM / 32;       // activation uint4 per thread per K step
+  constexpr int TPR = 8 / AV;       // threads per activation row
+  __shared__ uint4 As[2][BM * 8];   // [BM][64] bf16, swizzled, two buffers
+  const int K = GU ? g.H : g.I, N = GU ? g.I : g.H;
+  int tile, slice;
+  block_tile(N / NB, tile, slice);
+  int e, r0, r1;
+  if (!tile_of(g, tile, e, r0, r1)) return;
+  const int n0 = slice * NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  // activation rows (rows past the tile's end load a valid row; never stored)
+  const int a_row = tid / TPR, a_c0 = (tid % TPR) * AV;
+  const int arow = min(r0 + a_row, r1 - 1);
+  const u32x4_t* asrc;
+  if (GU) {
+    const int tok = g.sorted_pairs ? g.sorted_pairs[arow] / g.k : arow;
+    asrc = (const u32x4_t*)(g.x + (size_t)tok * K) + a_c0;
+  } else {
+    asrc = (const u32x4_t*)(g.h + (size_t)arow * K) + a_c0;
+  }
+  // this lane's two B columns
+  const uint8_t* bcp[2];
+  const uint8_t* bsp[2];
+  const uint8_t* bzp[2];
+#pragma unroll
+  for (int cf = 0; cf < 2; ++cf) {
+    const size_t row = GU ? (size_t)e * N + n0 + wave * 32 + l32 : (size_t)e * N + n0 + wave * 64 + cf * 32 + l32;
+    const uint8_t* codes = GU ? (cf ? g.uc : g.gc) : g.dc;
+    const uint8_t* scales = GU ? (cf ? g.us : g.gs) : g.ds;
+    const uint8_t* zeros = GU ? (cf ? g.uz : g.gz) : g.dz;
+    bcp[cf] = codes + row * (K / 2) + hf * 16;
+    if (NV) {
+      bsp[cf] = scales + row * (K / 16);  // both halves' scales: 16 bytes per 4 steps
+      bzp[cf] = nullptr;
+    } else {
+      bsp[cf] = scales + row * (K / 64) * 2;
+      bzp[cf] = zeros + row * (K / 64);
+    }
+  }
+  // Plain vectors, not uint4: a struct copy from global memory becomes a
+  // block copy through private memory.  Activations: ring of D steps.
+  u32x4_t ar[AV][D];
+  // NVFP4 weights: two groups of 4 steps (codes, 16 scale bytes per column)
+  u32x4_t gq[2][4][2];
+  u32x4_t gsv[2][2];
+  // INT4 weights: ring of D steps
+  u32x4_t bq[D][2];
+  int bz[D][2];
+  float bgs[D][2];
+  auto load_a = [&](int kt, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) ar[v][j] = asrc[kt * 8 + v];
+  };
+  auto load_group = [&](int kt0, int grp) __attribute__((always_inline)) {  // NVFP4, steps kt0 .. kt0 + 3
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gq[grp][j][cf] = *(const u32x4_t*)(bcp[cf] + (kt0 + j) * 32);
+      gsv[grp][cf] = *(const u32x4_t*)(bsp[cf] + kt0 * 4);
+    }
+  };
+  auto load_b = [&](int kt, int j) __attribute__((always_inline)) {  // INT4, one step
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+      bq[j][cf] = *(const u32x4_t*)(bcp[cf] + kt * 32);
+      bz[j][cf] = bzp[cf][kt];
+      bgs[j][cf] = f16_to_f32(((const uint16_t*)bsp[cf])[kt]);
+    }
+  };
+  auto write_a = [&](int j, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) ((u32x4_t*)As[buf])[swz(a_row, a_c0 + v)] = ar[v][j];
+  };
+
+  f32x16_t acc[2][RF];
+#pragma unroll
+  for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) acc[cf][rf] = f32x16_t{};
+
+  const int nk = K / kBK;
+  // loads past the last K step repeat it (in bounds, never used)
+  load_a(0, 0);
+  if (NV) {
+    load_group(0, 0);
+    if (4 < nk) load_group(4, 1);
+  } else {
+    load_b(0, 0);
+  }
+  load_a(min(1, nk - 1), 1);
+  if (!NV) load_b(min(1, nk - 1), 1);
+  load_a(min(2, nk - 1), 2);
+  if (!NV) load_b(min(2, nk - 1), 2);
+  load_a(min(3, nk - 1), 3);
+  if (!NV) load_b(min(3, nk - 1), 3);
+  write_a(0, 0);
+  __syncthreads();
+  auto step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int kt = decltype(kc)::value, j = kt % D, grp = (kt / 4) & 1;
+    write_a((j + 1) % D, (kt + 1) & 1);  // after the last step: unused
+    uint4 o[2][4];
+    float s0 = 1.f, s1 = 1.f;
+    if (NV) {
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf) {
+        const uint32_t sc = gsv[grp][cf][j] >> (16 * hf);  // this half's two block scales
+        dequant32<FMT>(to_uint4(gq[grp][j][cf]), sc, 0, o[cf]);
+      }
+    } else {
+      dequant32<FMT>(to_uint4(bq[j][0]), 0, bz[j][0], o[0]);
+      dequant32<FMT>(to_uint4(bq[j][1]), 0, bz[j][1], o[1]);
+      s0 = bgs[j][0];
+      s1 = bgs[j][1];
+    }
+    load_a(min(kt + D, nk - 1), j);
+    if (NV) {
+      if (j == 0 && kt + 4 < nk && kt >= 4) load_group(kt + 4, grp ^ 1);
+    } else {
+      load_b(min(kt + D, nk - 1), j);
+    }
+    const uint4* at = As[kt & 1];
+    f32x16_t part[2][RF];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) part[cf][rf] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t a[RF];
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) a[rf] = lds_frag(at, rf * 32 + l32, hf * 4 + ks);
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, o[cf][ks]);
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf) {
+          if (NV)
+            acc[cf][rf] = mfma(a[rf], b, acc[cf][rf]);
+          else
+            part[cf][rf] = mfma(a[rf], b, part[cf][rf]);
+        }
+      }
+    }
+    if (!NV) {
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          acc[0][rf][i] = fmaf(s0, part[0][rf][i], acc[0][rf][i]);
+          acc[1][rf][i] = fmaf(s1, part[1][rf][i], acc[1][rf][i]);
+        }
+    }
+    __syncthreads();
+  };
+  // Straight-line code (no loop back edge): the compiler then waits for each
+  // step's own loads only, not for every load in flight.
+  unrolled_steps<0, kBdMaxSteps>(nk, step);
+  if (GU) {
+    const float tsg = NV ? g.gts[e] : 1.f, tsu = NV ? g.uts[e] : 1.f;
+    const int f = n0 + wave * 32 + l32;
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = rf * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+        if (r0 + row < r1) {
+          const float gv = acc[0][rf][i] * tsg, uv = acc[1][rf][i] * tsu;
+          g.h[(size_t)(r0 + row) * N + f] = (uint16_t)f32_to_bf16_rne(silu_f32(gv) * uv);
+        }
+      }
+    }
+  } else {
+    const float ts = NV ? g.dts[e] : 1.f;
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+      const int col = n0 + wave * 64 + cf * 32 + l32;
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = rf * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+          if (r0 + row < r1) g.out[(size_t)(r0 + row) * N + col] = acc[cf][rf][i] * ts;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ router (large batches)
 // logits[t, e] = sum_h x[t, h] * w[e, h] on the matrix cores.  Each fp32
 // router weight is split exactly into three bf16 parts, w = hi + mid + lo
@@ -616,16 +847,30 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   gs.tiles = small;
   gs.tile_rows = 64;
   const bool nv = w->gate.fmt == kFmtNvfp4;
+  const bool bd = split && bd_k_ok(w->gate.fmt, H) && bd_k_ok(w->gate.fmt, I);
+  const dim3 gu_small(small8 * (I / 128)), dn_small(small8 * (H / 256));
   if (nv) {
     hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), dim3(small8 * (I / 128)), dim3(256), 0, s, gs);
+    if (bd)
+      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, true>), gu_small, dim3(256), 0, s, gs);
+    else if (split)
+      hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), gu_small, dim3(256), 0, s, gs);
     hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dim3(small8 * (H / 256)), dim3(256), 0, s, gs);
+    if (bd)
+      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, false>), dn_small, dim3(256), 0, s, gs);
+    else if (split)
+      hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dn_small, dim3(256), 0, s, gs);
   } else {
     hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), dim3(small8 * (I / 128)), dim3(256), 0, s, gs);
+    if (bd)
+      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, true>), gu_small, dim3(256), 0, s, gs);
+    else if (split)
+      hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), gu_small, dim3(256), 0, s, gs);
     hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dim3(small8 * (H / 256)), dim3(256), 0, s, gs);
+    if (bd)
+      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, false>), dn_small, dim3(256), 0, s, gs);
+    else if (split)
+      hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dn_small, dim3(256), 0, s, gs);
   }
   return hipGetLastError();
 }

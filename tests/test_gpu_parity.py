@@ -342,7 +342,21 @@ LAYER_CASES = [
     ("one_expert_k1", 1, 256, 128, 1, 1, 9, 8, False),
     ("k8_E16", 2, 256, 192, 16, 8, 13, 9, True),
     ("ragged_H192_I320", 1, 192, 320, 8, 3, 9, 10, True),
+    ("flint_int4_T1", 2, 2048, 768, 256, 6, 1, 12, True),
+    ("tiny_nvfp4_T1_k8", 1, 256, 128, 16, 8, 1, 13, True),
+    ("tiny_int4_T1_k8", 2, 256, 128, 16, 8, 1, 14, False),
 ]
+
+
+@pytest.mark.parametrize("shared,I_shared,T", [(False, None, 1), (False, None, 4), (True, 256, 1), (True, 256, 5)])
+def test_layer_decode_shared_variants(shared, I_shared, T):
+    """No shared expert, or a shared expert wider than the routed ones (the
+    single-token down kernel needs equal widths and the layer falls back)."""
+    print("shared variants", shared, I_shared, T, flush=True)
+    layer = synth.make_layer(1, 256, 128, 32, 6, 40 + T, DEV, shared=shared, I_shared=I_shared)
+    x = synth.make_tokens(T, 256, 40 + T, DEV)
+    y, ids, w = run_layer(layer, x, x, T)
+    check_layer(layer, x, x, y, ids, w)
 
 
 @pytest.mark.parametrize("name,fmt,H,I,E,k,T,seed,res", LAYER_CASES)

@@ -8,13 +8,15 @@
 //   gate/up kernel: G = X_e Wg_e^T, U = X_e Wu_e^T over K = H, then
 //                   h = bf16(silu(G) * U);
 //   down kernel:    O = h_e Wd_e^T over K = I, fp32.
-// A device-side table lists (expert, first row) for every 128-row tile.
-// When the shapes allow, an expert's final remainder of at most 64 rows goes
-// to a second table of 64-row tiles (4 waves side by side instead of 2 x 2):
-// with Zipf-skewed routing most experts get a few dozen rows, and a 128-row
-// tile would spend half of its matrix work and LDS traffic on padding.
+// A device-side table lists (expert, first row) for every row tile.
+// Main path (k_mfma_bd): 64-row tiles; each lane streams its own weight
+// column from HBM into registers and dequantises it there.  With Zipf-skewed
+// routing most experts get a few dozen rows, so small tiles waste little
+// matrix work on padding.  Other shapes: 128-row tiles with the weights
+// dequantised into LDS, and an expert's final remainder of at most 64 rows
+// in a 64-row tile (4 waves side by side instead of 2 x 2).
 //
-// Weights are dequantised once per 64-wide K step into LDS as bf16:
+// Weights are dequantised once per 64-wide K step, as bf16:
 //   NVFP4: e4m3 * e2m1 has at most 6 significant bits, so the bf16 operand is
 //          exact; the fp32 tensor scale multiplies the accumulator at the end;
 //   INT4:  the operand is the exact integer (q - z); each 64-wide K step is one
@@ -116,8 +118,8 @@ MOE_DEV bool tile_of(const MfmaArgs& g, int mt, int& e, int& r0, int& r1) {
 // Tile tables, one block: each expert's rows in 128-row tiles (`big`); with
 // `split`, a final remainder of 1..64 rows becomes one 64-row tile (`small`)
 // instead.  Each table: [0] = count, then (expert, first row) pairs.
-__global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__ offsets, int E, int rows, int split,
-                                                     int32_t* __restrict__ big, int32_t* __restrict__ small) {
+__global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__ offsets, int E, int rows, int bm,
+                                                     int split, int32_t* __restrict__ big, int32_t* __restrict__ small) {
   __shared__ int scan_lds[17];
   const int e = threadIdx.x;
   int r0 = 0, r1 = 0;
@@ -125,20 +127,20 @@ __global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__
     r0 = offsets ? offsets[e] : 0;
     r1 = offsets ? offsets[e + 1] : rows;
   }
-  const int c = r1 - r0, rem = c % kBM;
+  const int c = r1 - r0, rem = c % bm;
   const bool to_small = split && rem > 0 && rem <= 64;
-  const int nb = c / kBM + ((rem > 0 && !to_small) ? 1 : 0);
+  const int nb = c / bm + ((rem > 0 && !to_small) ? 1 : 0);
   const int ns = to_small ? 1 : 0;
   int tb, ts;
   const int fb = block_exclusive_scan(nb, scan_lds, tb);
   const int fs = block_exclusive_scan(ns, scan_lds, ts);
   for (int t = 0; t < nb; ++t) {
     big[1 + 2 * (fb + t)] = e;
-    big[2 + 2 * (fb + t)] = r0 + t * kBM;
+    big[2 + 2 * (fb + t)] = r0 + t * bm;
   }
   if (ns) {
     small[1 + 2 * fs] = e;
-    small[2 + 2 * fs] = r0 + (c / kBM) * kBM;
+    small[2 + 2 * fs] = r0 + (c / bm) * bm;
   }
   if (e == 0) {
     big[0] = tb;
@@ -163,6 +165,19 @@ __global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__
 // Map the block index to (row tile, column slice) so that every column slice
 // of a row tile runs on the same XCD (blocks go to XCDs round-robin), and the
 // tile's activation rows stay in that XCD's L2.
+// Contiguous tile ranges per XCD: XCD x takes tiles [x * per, (x + 1) * per)
+// in order, each with all its column slices back to back.  Neighbouring row
+// tiles of one expert then run on the same XCD at about the same time and
+// read that expert's weights from its L2 after the first.  A block whose tile
+// is past the table's end returns (tile_of).
+MOE_DEV void block_tile_chunked(int nslices, int ntiles, int& tile, int& slice) {
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int per = (ntiles + 7) >> 3;
+  const int t = j / nslices;
+  tile = t < per ? xcd * per + t : 0x7fffffff;
+  slice = j % nslices;
+}
+
 MOE_DEV void block_tile(int nslices, int& tile, int& slice) {
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   tile = (j / nslices) * 8 + xcd;
@@ -455,6 +470,25 @@ __global__ void __launch_bounds__(256, (WM == 1 && FMT == kFmtNvfp4) ? 3 : 2) k_
 // !GU: columns n0 + wave*64 + cf*32 + l%32 (the block covers 256 outputs).
 constexpr int kBdMaxSteps = 32;  // K <= 2048
 
+#ifdef MOE_TRACE
+// Per-block phase timestamps (100 MHz constant clock) for development builds.
+__device__ unsigned long long g_trace_bd[2][65536 * 8];
+#define MOE_TRACE_BD(kern, slot)                                                      \
+  do {                                                                                \
+    if (threadIdx.x == 0 && blockIdx.x < 65536)                                       \
+      g_trace_bd[kern][blockIdx.x * 8 + (slot)] = __builtin_amdgcn_s_memrealtime();   \
+  } while (0)
+extern "C" void* moe_trace_bd_ptr() {
+  void* p = nullptr;
+  (void)hipGetSymbolAddress(&p, HIP_SYMBOL(g_trace_bd));
+  return p;
+}
+#else
+#define MOE_TRACE_BD(kern, slot) \
+  do {                           \
+  } while (0)
+#endif
+
 // f(kt) for kt = KT .. nk - 1 as compile-time constants, written out.
 template <int KT, int NMAX, class F>
 MOE_DEV void unrolled_steps(int nk, F& f) {
@@ -479,9 +513,10 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   __shared__ uint4 As[2][BM * 8];   // [BM][64] bf16, swizzled, two buffers
   const int K = GU ? g.H : g.I, N = GU ? g.I : g.H;
   int tile, slice;
-  block_tile(N / NB, tile, slice);
+  block_tile_chunked(N / NB, g.tiles[0], tile, slice);
   int e, r0, r1;
   if (!tile_of(g, tile, e, r0, r1)) return;
+  MOE_TRACE_BD(GU ? 0 : 1, 0);
   const int n0 = slice * NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // activation rows (rows past the tile's end load a valid row; never stored)
@@ -571,6 +606,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   if (!NV) load_b(min(3, nk - 1), 3);
   write_a(0, 0);
   __syncthreads();
+  MOE_TRACE_BD(GU ? 0 : 1, 1);
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int kt = decltype(kc)::value, j = kt % D, grp = (kt / 4) & 1;
     write_a((j + 1) % D, (kt + 1) & 1);  // after the last step: unused
@@ -627,10 +663,15 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
         }
     }
     __syncthreads();
+    if (kt == 0) MOE_TRACE_BD(GU ? 0 : 1, 2);
+    if (kt == 3) MOE_TRACE_BD(GU ? 0 : 1, 3);
+    if (kt == 7) MOE_TRACE_BD(GU ? 0 : 1, 4);
+    if (kt == 11) MOE_TRACE_BD(GU ? 0 : 1, 5);
   };
   // Straight-line code (no loop back edge): the compiler then waits for each
   // step's own loads only, not for every load in flight.
   unrolled_steps<0, kBdMaxSteps>(nk, step);
+  MOE_TRACE_BD(GU ? 0 : 1, 6);
   if (GU) {
     const float tsg = NV ? g.gts[e] : 1.f, tsu = NV ? g.uts[e] : 1.f;
     const int f = n0 + wave * 32 + l32;
@@ -792,7 +833,7 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, 
   return hipGetLastError();
 }
 
-static size_t big_tiles_max(int E, int total_rows) { return (size_t)total_rows / kBM + E + 1; }
+static size_t big_tiles_max(int E, int total_rows) { return (size_t)total_rows / 64 + E + 1; }
 static size_t tables_bytes(int E, int total_rows) {
   const size_t t = (1 + 2 * big_tiles_max(E, total_rows) + 1 + 2 * ((size_t)E + 1)) * sizeof(int32_t);
   return (t + 255) & ~(size_t)255;
@@ -838,7 +879,25 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.dts = w->down.tensor_scale;
   g.h = h;
   g.out = out;
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, split ? 1 : 0, big, small);
+  // Weights streamed into registers (k_mfma_bd): every tile is 64 rows.
+  if (split && bd_k_ok(w->gate.fmt, H) && bd_k_ok(w->gate.fmt, I)) {
+    hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, 64, 0, big, small);
+    const unsigned b8 = (unsigned)((max_big + 7) / 8 * 8);
+    MfmaArgs ga = g;
+    ga.tiles = big;
+    ga.tile_rows = 64;
+    if (w->gate.fmt == kFmtNvfp4) {
+      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
+      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
+    } else {
+      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
+      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
+    }
+    return hipGetLastError();
+  }
+  // Otherwise LDS-staged weights: 128-row tiles, with a final remainder of at
+  // most 64 rows in a 64-row tile when the shapes allow.
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, kBM, split ? 1 : 0, big, small);
   // one block per (row tile, column slice); tiles rounded up to a multiple of the 8 XCDs
   const unsigned big8 = (unsigned)((max_big + 7) / 8 * 8), small8 = (unsigned)((E + 7) / 8 * 8);
   MfmaArgs gb = g, gs = g;
@@ -846,31 +905,17 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   gb.tile_rows = kBM;
   gs.tiles = small;
   gs.tile_rows = 64;
-  const bool nv = w->gate.fmt == kFmtNvfp4;
-  const bool bd = split && bd_k_ok(w->gate.fmt, H) && bd_k_ok(w->gate.fmt, I);
   const dim3 gu_small(small8 * (I / 128)), dn_small(small8 * (H / 256));
-  if (nv) {
+  if (w->gate.fmt == kFmtNvfp4) {
     hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (bd)
-      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, true>), gu_small, dim3(256), 0, s, gs);
-    else if (split)
-      hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), gu_small, dim3(256), 0, s, gs);
+    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), gu_small, dim3(256), 0, s, gs);
     hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (bd)
-      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, false>), dn_small, dim3(256), 0, s, gs);
-    else if (split)
-      hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dn_small, dim3(256), 0, s, gs);
+    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dn_small, dim3(256), 0, s, gs);
   } else {
     hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (bd)
-      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, true>), gu_small, dim3(256), 0, s, gs);
-    else if (split)
-      hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), gu_small, dim3(256), 0, s, gs);
+    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), gu_small, dim3(256), 0, s, gs);
     hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (bd)
-      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, false>), dn_small, dim3(256), 0, s, gs);
-    else if (split)
-      hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dn_small, dim3(256), 0, s, gs);
+    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dn_small, dim3(256), 0, s, gs);
   }
   return hipGetLastError();
 }

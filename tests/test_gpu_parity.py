@@ -463,6 +463,7 @@ MFMA_CASES = [
     # fmt, H, I, E, k, T, seed, routing
     (2, 256, 128, 32, 6, 64, 100, "uniform"),
     (1, 256, 192, 8, 3, 300, 101, "zipf"),       # several 128-row tiles per expert, ragged tails
+    (1, 256, 384, 16, 4, 200, 104, "zipf"),      # LDS-staged 128-row tiles with 64-row remainders
     (1, 2048, 768, 256, 6, 512, 102, "zipf"),
     (2, 2048, 768, 256, 6, 512, 103, "zipf"),
 ]

@@ -509,7 +509,6 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   constexpr bool NV = FMT == kFmtNvfp4;
   constexpr int BM = 32 * RF, D = 4, NB = GU ? 128 : 256;
   constexpr int AV = BM / 32;       // activation uint4 per thread per K step
-  constexpr int TPR = 8 / AV;       // threads per activation row
   __shared__ uint4 As[2][BM * 8];   // [BM][64] bf16, swizzled, two buffers
   const int K = GU ? g.H : g.I, N = GU ? g.I : g.H;
   int tile, slice;
@@ -519,15 +518,20 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   MOE_TRACE_BD(GU ? 0 : 1, 0);
   const int n0 = slice * NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  // activation rows (rows past the tile's end load a valid row; never stored)
-  const int a_row = tid / TPR, a_c0 = (tid % TPR) * AV;
-  const int arow = min(r0 + a_row, r1 - 1);
-  const u32x4_t* asrc;
-  if (GU) {
-    const int tok = g.sorted_pairs ? g.sorted_pairs[arow] / g.k : arow;
-    asrc = (const u32x4_t*)(g.x + (size_t)tok * K) + a_c0;
-  } else {
-    asrc = (const u32x4_t*)(g.h + (size_t)arow * K) + a_c0;
+  // Activations: load v of a thread is row v * 32 + tid / 8, 16-byte chunk
+  // tid % 8, so 8 lanes read one row's 128 bytes of a K step.  Rows past the
+  // tile's end load a valid row; their outputs are never stored.
+  const int a_chunk = tid & 7;
+  const u32x4_t* asrc[AV];
+#pragma unroll
+  for (int v = 0; v < AV; ++v) {
+    const int arow = min(r0 + v * 32 + (tid >> 3), r1 - 1);
+    if (GU) {
+      const int tok = g.sorted_pairs ? g.sorted_pairs[arow] / g.k : arow;
+      asrc[v] = (const u32x4_t*)(g.x + (size_t)tok * K) + a_chunk;
+    } else {
+      asrc[v] = (const u32x4_t*)(g.h + (size_t)arow * K) + a_chunk;
+    }
   }
   // this lane's two B columns
   const uint8_t* bcp[2];
@@ -560,7 +564,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   float bgs[D][2];
   auto load_a = [&](int kt, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) ar[v][j] = asrc[kt * 8 + v];
+    for (int v = 0; v < AV; ++v) ar[v][j] = asrc[v][kt * 8];
   };
   auto load_group = [&](int kt0, int grp) __attribute__((always_inline)) {  // NVFP4, steps kt0 .. kt0 + 3
 #pragma unroll
@@ -580,7 +584,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   };
   auto write_a = [&](int j, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) ((u32x4_t*)As[buf])[swz(a_row, a_c0 + v)] = ar[v][j];
+    for (int v = 0; v < AV; ++v) ((u32x4_t*)As[buf])[swz(v * 32 + (tid >> 3), a_chunk)] = ar[v][j];
   };
 
   f32x16_t acc[2][RF];

@@ -37,7 +37,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_BYTES = {
     ("decode_b1", "nvfp4"): 22.00e6,
     ("decode_T16", "nvfp4"): 223.8e6,
-    ("prefill", "nvfp4"): 1386.5e6,
+    ("prefill", "nvfp4"): 1250.6e6,
 }
 
 
@@ -322,7 +322,7 @@ def bench_prefill(args, fmt):
         "roofline": {"bound": "mfma", "achieved": flops / (ms_ffn / K * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ms_ffn / K * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": TRAFFIC_BYTES.get(("prefill", args.fmt)),
-                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, k_mfma_gateup, k_mfma_down"},
+                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, k_mfma_bd gate/up, k_mfma_bd down"},
         "cpu_baseline": None,
     }
     print(json.dumps(out_line))

@@ -225,8 +225,11 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
                     "moe_permute");
 }
 
-// MFMA when the average expert gets enough rows to fill matrix-core tiles.
-constexpr int kAutoMfmaRowsPerExpert = 16;
+// MFMA once the experts average two rows: the matrix-core kernel streams each
+// touched expert's weights once per 64-row tile, as the GEMV path does, and
+// its extra rows are nearly free (measured crossover: 64 decode tokens, top-6
+// of 256 experts).
+constexpr int kAutoMfmaRowsPerExpert = 2;
 
 static bool use_mfma(int mode, int E, int H, int I, int total_rows) {
   if (mode == MOE_MODE_MFMA) return true;

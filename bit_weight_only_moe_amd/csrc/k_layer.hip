@@ -325,6 +325,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   uint64_t* rk = (uint64_t*)(((uintptr_t)(cand_e + 32) + 15) & ~(uintptr_t)15);  // [kRankScratch]
   copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
   __syncthreads();
+  if (nb == 1) MOE_TRACE_AT(0, 7);
   // a lone token: all four waves share its selection (rank counting for up
   // to 256 experts); several tokens: one per wave
   if (nt == 1 && E <= 256)

@@ -468,8 +468,8 @@ __global__ void __launch_bounds__(256) k_layer_gateup(LayerArgs a) {
 }
 
 // ------------------------------------------------------------------ launch 3
-// One (unit, 64-row slice of H) per block; units are the routed records,
-// then the shared expert's token batches.  fp32 outputs go to the
+// One (unit, 64-row slice of H) per block; units are the shared expert's
+// token batches, then the routed records.  fp32 outputs go to the
 // workspace; the last block of each slice combines
 // y = residual + sum_j w_j o_j + o_shared in that fixed order.
 template <int FMT, int NT>
@@ -480,8 +480,11 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   MOE_TRACE_AT(2, 0);
   const int tid = threadIdx.x;
   const int T = a.T, H = a.H, k = a.k, n = T * k;
-  const int slice = blockIdx.x % a.slices_d, unit = blockIdx.x / a.slices_d;
-  const bool routed = unit < a.max_active;
+  // the shared expert's units come first: they carry NT tokens each and
+  // would otherwise be the launch's tail
+  const int slice = blockIdx.x % a.slices_d, u = blockIdx.x / a.slices_d;
+  const bool routed = u >= a.nsb;
+  const int unit = routed ? u - a.nsb : u;
   // the combine's weights and pair positions (written by launch 1), loaded
   // with the record so the last block needs one more round trip only
   float* s_w = (float*)(smem + a.down_stage_bytes);  // [n]
@@ -501,7 +504,7 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     down_rows<FMT, NT>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed, a.o_routed, a.lpr_i, true,
                        smem);
   } else {
-    const int r0 = (unit - a.max_active) * NT;
+    const int r0 = unit * NT;
     down_rows<FMT, NT>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared, a.lpr_is, true, smem);
   }
   MOE_TRACE_AT(2, 3);

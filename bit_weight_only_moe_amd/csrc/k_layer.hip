@@ -48,11 +48,24 @@ __device__ unsigned long long g_trace[3][65536 * 8];
   } while (0)
 #endif
 
-constexpr int kRG = 16;      // gate/up rows per block (4 when T == 1)
-constexpr int kRD = 64;      // down rows per block (32 when T == 1)
+#ifndef MOE_RG_MULTI
+#define MOE_RG_MULTI 16
+#endif
+#ifndef MOE_PCG_MULTI
+#define MOE_PCG_MULTI 4
+#endif
+#ifndef MOE_RD_MULTI
+#define MOE_RD_MULTI 64
+#endif
+#ifndef MOE_PCD_MULTI
+#define MOE_PCD_MULTI 8
+#endif
+constexpr int kRG = MOE_RG_MULTI;   // gate/up rows per block (4 when T == 1)
+constexpr int kRD = MOE_RD_MULTI;   // down rows per block (32 when T == 1)
 constexpr int kRDMin = 32;   // smallest down slice: bounds the number of slice tickets
-constexpr int kMaxPcG = 4;   // gate/up weight pieces per lane held in registers, per matrix
-constexpr int kMaxPcD = 8;   // down weight pieces per lane held in registers
+// weight pieces per lane held in registers (gate/up: per matrix), by tokens per batch
+template <int NT> constexpr int kMaxPcG = NT == 1 ? 4 : MOE_PCG_MULTI;
+template <int NT> constexpr int kMaxPcD = NT == 1 ? 8 : MOE_PCD_MULTI;
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
@@ -99,11 +112,11 @@ struct LayerArgs {
 // ------------------------------------------------------------------ gate/up
 // Load this lane's pieces c0 .. c0+kMaxPcG-1 (row iteration c / ppl, piece
 // c % ppl) of the gate and up rows into registers.
-template <int FMT>
+template <int FMT, int PC>
 MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, int npc, int ppl, int lpr, int lir,
-                               int row0, int row_step, int i1, RawPiece (&rg)[kMaxPcG], RawPiece (&ru)[kMaxPcG]) {
+                               int row0, int row_step, int i1, RawPiece (&rg)[PC], RawPiece (&ru)[PC]) {
 #pragma unroll
-  for (int q = 0; q < kMaxPcG; ++q) {
+  for (int q = 0; q < PC; ++q) {
     const int c = c0 + q;
     const int i = row0 + row_step * (c / ppl);
     if (c < npc && i < i1) {
@@ -130,10 +143,11 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
   const float tsg = tensor_scale<FMT>(G, e), tsu = tensor_scale<FMT>(U, e);
   // When every piece fits in registers they are loaded once, before the
   // tokens are staged, so both memory latencies overlap.
-  const bool resident = npc <= kMaxPcG;
-  RawPiece rg[kMaxPcG], ru[kMaxPcG];
+  constexpr int PC = kMaxPcG<NT>;
+  const bool resident = npc <= PC;
+  RawPiece rg[PC], ru[PC];
   const int row0 = i0 + wave * rpw + rsub;
-  if (resident) load_gateup_chunk<FMT>(G, U, e, 0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
+  if (resident) load_gateup_chunk<FMT, PC>(G, U, e, 0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
   for (int rb = r0; rb < r1; rb += NT) {
     const int nt = min(NT, r1 - rb);
     __syncthreads();
@@ -143,11 +157,11 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
     float ag[NT], au[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
-    for (int c0 = 0; c0 < npc; c0 += kMaxPcG) {
+    for (int c0 = 0; c0 < npc; c0 += PC) {
       // piece c of this lane: row iteration c / ppl, piece index c % ppl
-      if (!resident) load_gateup_chunk<FMT>(G, U, e, c0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
+      if (!resident) load_gateup_chunk<FMT, PC>(G, U, e, c0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
 #pragma unroll
-      for (int q = 0; q < kMaxPcG; ++q) {
+      for (int q = 0; q < PC; ++q) {
         const int c = c0 + q;
         if (c < npc) {
           const int i = row0 + 4 * rpw * (c / ppl);
@@ -196,12 +210,13 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   uint16_t* xs = (uint16_t*)smem;
   float* xsum = (float*)(smem + (size_t)NT * K * sizeof(uint16_t));
   const float ts = tensor_scale<FMT>(D, e);
-  const bool resident = npc <= kMaxPcD;  // every piece stays in registers across token batches
+  constexpr int PC = kMaxPcD<NT>;
+  const bool resident = npc <= PC;  // every piece stays in registers across token batches
   const int row0 = n0 + wave * rpw + rsub;
-  RawPiece rd[kMaxPcD];
+  RawPiece rd[PC];
   if (resident) {
 #pragma unroll
-    for (int q = 0; q < kMaxPcD; ++q) {
+    for (int q = 0; q < PC; ++q) {
       const int n = row0 + 4 * rpw * (q / ppl);
       if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
                                                       lir + (q % ppl) * lpr);
@@ -216,10 +231,10 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-    for (int c0 = 0; c0 < npc; c0 += kMaxPcD) {
+    for (int c0 = 0; c0 < npc; c0 += PC) {
       if (!resident) {
 #pragma unroll
-        for (int q = 0; q < kMaxPcD; ++q) {
+        for (int q = 0; q < PC; ++q) {
           const int c = c0 + q;
           const int n = row0 + 4 * rpw * (c / ppl);
           if (c < npc && n < n1)
@@ -228,7 +243,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
         }
       }
 #pragma unroll
-      for (int q = 0; q < kMaxPcD; ++q) {
+      for (int q = 0; q < PC; ++q) {
         const int c = c0 + q;
         if (c < npc) {
           const int n = row0 + 4 * rpw * (c / ppl);
@@ -314,15 +329,22 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   __syncthreads();
   MOE_TRACE_AT(0, 5);
   const int k = a.k, n = T * k;
-  int32_t* s_ids = (int32_t*)smem;                                      // [n]
-  float* s_w = (float*)(s_ids + n);                                     // [n]
-  float* s_log = s_w + n;                                               // [kRouteT, E]
-  unsigned long long* mask = (unsigned long long*)(((uintptr_t)(s_log + kRouteT * E) + 7) & ~(uintptr_t)7);  // [E]
-  int32_t* off = (int32_t*)(mask + E);                                  // [E + 1]
-  int* scan_tmp = (int*)(off + E + 1);                                  // [17]
-  float* cand_v = (float*)(scan_tmp + 17);                              // [4 * 8]
-  int32_t* cand_e = (int32_t*)(cand_v + 32);                            // [4 * 8]
-  uint64_t* rk = (uint64_t*)(((uintptr_t)(cand_e + 32) + 15) & ~(uintptr_t)15);  // [kRankScratch]
+  // Byte offsets into smem: pointers formed as smem + offset stay LDS
+  // pointers for the compiler (an integer round trip would turn every access
+  // below into a slower flat access).
+  const int o_w = 4 * n, o_log = 8 * n;
+  const int o_mask = (o_log + 4 * kRouteT * E + 7) & ~7, o_off = o_mask + 8 * E;
+  const int o_scan = o_off + 4 * (E + 1), o_cv = o_scan + 4 * 17, o_ce = o_cv + 4 * 32;
+  const int o_rk = (o_ce + 4 * 32 + 15) & ~15;
+  int32_t* s_ids = (int32_t*)smem;                                // [n]
+  float* s_w = (float*)(smem + o_w);                              // [n]
+  float* s_log = (float*)(smem + o_log);                          // [kRouteT, E]
+  unsigned long long* mask = (unsigned long long*)(smem + o_mask);  // [E]
+  int32_t* off = (int32_t*)(smem + o_off);                        // [E + 1]
+  int* scan_tmp = (int*)(smem + o_scan);                          // [17]
+  float* cand_v = (float*)(smem + o_cv);                          // [4 * 8]
+  int32_t* cand_e = (int32_t*)(smem + o_ce);                      // [4 * 8]
+  uint64_t* rk = (uint64_t*)(smem + o_rk);                        // [kRankScratch]
   copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
   __syncthreads();
   if (nb == 1) MOE_TRACE_AT(0, 7);

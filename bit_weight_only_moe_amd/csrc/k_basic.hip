@@ -97,9 +97,14 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H
 // ---------------------------------------------------------------- top-k + softmax
 __global__ void __launch_bounds__(256) k_topk_softmax(const float* __restrict__ logits, int T, int E, int k,
                                                       int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __align__(16) uint64_t scratch[4 * kWaveRankScratch];
+  const int wave = threadIdx.x >> 6, t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  wave_topk_softmax(logits + (size_t)t * E, E, k, threadIdx.x & 63, ids + (size_t)t * k, w + (size_t)t * k);
+  if (E <= 256)
+    wave_topk_rank(logits + (size_t)t * E, E, k, threadIdx.x & 63, scratch + wave * kWaveRankScratch,
+                   ids + (size_t)t * k, w + (size_t)t * k);
+  else
+    wave_topk_softmax(logits + (size_t)t * E, E, k, threadIdx.x & 63, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {

@@ -101,6 +101,7 @@ struct LayerArgs {
   int nRe, nR;               // router blocks: expert groups of 4, total (expert groups x token batches)
   int nsb;                   // shared-expert token batches of NT tokens (0: no shared expert)
   int rg, rd;                // rows per gate/up block, per down block
+  int rgs;                   // rows per shared-expert gate/up block
   int ss_r;                  // shared gate/up row slices
   int slices_r;              // routed gate/up row slices per expert
   int slices_d;              // down row slices of H
@@ -286,7 +287,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   if ((int)blockIdx.x >= a.nR) {
     const int b = blockIdx.x - a.nR;
     const int slice = b % a.ss_r, r0 = (b / a.ss_r) * NT;
-    const int i0 = slice * a.rg, i1 = min(a.Is, i0 + a.rg);
+    const int i0 = slice * a.rgs, i1 = min(a.Is, i0 + a.rgs);
     gateup_rows<FMT, NT>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x, [](int r) { return r; },
                          a.h_shared, a.Is, a.lpr_h, smem, 0);
     MOE_TRACE_AT(0, 4);
@@ -349,11 +350,15 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   __syncthreads();
   if (nb == 1) MOE_TRACE_AT(0, 7);
   // a lone token: all four waves share its selection (rank counting for up
-  // to 256 experts); several tokens: one per wave
+  // to 256 experts); several tokens: one per wave (rank counting over the
+  // lanes' largest keys for up to 256 experts, else k rounds of a wave maximum)
   if (nt == 1 && E <= 256)
     block_topk_rank(s_log, E, k, rk, s_ids + t0 * k, s_w + t0 * k);
   else if (nt == 1)
     block_topk_softmax(s_log, E, k, wave, lane, cand_v, cand_e, s_ids + t0 * k, s_w + t0 * k);
+  else if (wave < nt && E <= 256)
+    wave_topk_rank(s_log + wave * E, E, k, lane, rk + wave * kWaveRankScratch, s_ids + (t0 + wave) * k,
+                   s_w + (t0 + wave) * k);
   else if (wave < nt)
     wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
   __syncthreads();
@@ -748,7 +753,13 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   // a single token has little work per block: smaller slices spread it over more CUs
   a.rg = T == 1 ? 4 : kRG;
   a.rd = T == 1 ? kRDMin : kRD;
-  a.ss_r = L->shared ? (a.Is + a.rg - 1) / a.rg : 0;
+#ifndef MOE_RGS
+#define MOE_RGS 4
+#endif
+  // The shared expert's blocks carry a whole token batch each: thin row
+  // slices spread that work over more CUs while the router runs.
+  a.rgs = T == 1 ? 4 : MOE_RGS;
+  a.ss_r = L->shared ? (a.Is + a.rgs - 1) / a.rgs : 0;
   a.slices_r = (a.I + a.rg - 1) / a.rg;
   a.slices_d = (a.H + a.rd - 1) / a.rd;
   a.lpr_h = lanes_per_row(a.H);

@@ -274,7 +274,10 @@ MOE_DEV void block_topk_softmax(const float* __restrict__ row, int E, int k, int
 // chunk's top k; stage 2 ranks those <= 32 candidates.  The selected values
 // and the softmax are those of the round-based selection, bit for bit
 // (a NaN-only pick has the value -inf there, and here).
-constexpr int kRankScratch = 296;  // u64 LDS words: 256 keys, 32 candidates, 8 winners
+constexpr int kWaveRankScratch = 104;  // u64 LDS words per wave: 64 heads, 32 candidates, 8 winners
+// u64 LDS words of a block's rank scratch: one token by the block (256 keys,
+// 32 candidates, 8 winners) or one token per wave (4 x kWaveRankScratch)
+constexpr int kRankScratch = 4 * kWaveRankScratch;
 
 MOE_DEV uint64_t topk_key(float v, int idx) {
   const uint32_t hi = (v == v) ? f32_order_key(v) : 0u;
@@ -342,6 +345,49 @@ MOE_DEV void block_topk_rank(const float* __restrict__ row, int E, int k, uint64
   if (tid < E && r < k) C[wave * k + r] = mine;
   __syncthreads();
   if (wave == 0) rank_finish(C, F, k, lane, ids_out, w_out);
+}
+
+// One token row of E <= 256 logits by one wave (lane l owns entries
+// i*64 + l).  Each lane sorts its 4 keys; a key among the k largest has at
+// most k - 1 larger keys, so its lane's largest key ranks below k among the
+// 64 lanes' largest keys.  The 4 keys of each such lane (at most 4k <= 32)
+// are the candidates; rank_finish ranks them.  W: kWaveRankScratch LDS words
+// of this wave (16-byte aligned).
+MOE_DEV void wave_topk_rank(const float* __restrict__ row, int E, int k, int lane, uint64_t* W, int32_t* ids_out,
+                            float* w_out) {
+  uint64_t q0, q1, q2, q3;
+  {
+    const int e0 = lane, e1 = 64 + lane, e2 = 128 + lane, e3 = 192 + lane;
+    q0 = e0 < E ? topk_key(row[e0], e0) : 0ull;
+    q1 = e1 < E ? topk_key(row[e1], e1) : 0ull;
+    q2 = e2 < E ? topk_key(row[e2], e2) : 0ull;
+    q3 = e3 < E ? topk_key(row[e3], e3) : 0ull;
+  }
+  auto cx = [](uint64_t& a, uint64_t& b) {  // a >= b afterwards
+    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+  };
+  cx(q0, q1);
+  cx(q2, q3);
+  cx(q0, q2);
+  cx(q1, q3);
+  cx(q1, q2);
+  uint64_t* heads = W;
+  uint64_t* C = W + 64;
+  uint64_t* F = W + 96;
+  heads[lane] = q0;
+  if (lane < 32) C[lane] = 0ull;
+  wave_lds_sync();
+  const int r = key_rank<64>(heads, q0);
+  if (q0 != 0ull && r < k) {
+    C[r * 4 + 0] = q0;
+    C[r * 4 + 1] = q1;
+    C[r * 4 + 2] = q2;
+    C[r * 4 + 3] = q3;
+  }
+  wave_lds_sync();
+  rank_finish(C, F, k, lane, ids_out, w_out);
 }
 
 // Exclusive prefix sum over a block of up to 1024 threads (all threads must

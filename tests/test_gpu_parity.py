@@ -76,7 +76,8 @@ def test_dequant_bit_exact(which):
 
 # ------------------------------------------------------------------ router
 
-@pytest.mark.parametrize("T,E,k", [(4096, 256, 6), (37, 32, 8), (5, 1, 1), (64, 1024, 6)])
+@pytest.mark.parametrize("T,E,k", [(4096, 256, 6), (37, 32, 8), (5, 1, 1), (64, 1024, 6), (50, 100, 6),
+                                   (33, 200, 8), (9, 257, 6)])
 def test_topk_softmax_bit_exact_ids(T, E, k):
     print("topk", T, E, k, flush=True)
     g = torch.Generator().manual_seed(T * 31 + E)

@@ -48,24 +48,13 @@ __device__ unsigned long long g_trace[3][65536 * 8];
   } while (0)
 #endif
 
-#ifndef MOE_RG_MULTI
-#define MOE_RG_MULTI 16
-#endif
-#ifndef MOE_PCG_MULTI
-#define MOE_PCG_MULTI 4
-#endif
-#ifndef MOE_RD_MULTI
-#define MOE_RD_MULTI 64
-#endif
-#ifndef MOE_PCD_MULTI
-#define MOE_PCD_MULTI 8
-#endif
-constexpr int kRG = MOE_RG_MULTI;   // gate/up rows per block (4 when T == 1)
-constexpr int kRD = MOE_RD_MULTI;   // down rows per block (32 when T == 1)
+// Rows per block (measured: 8 or 32 gate/up rows, 32 or 128 down rows are
+// slower from 4 to 64 tokens).
+constexpr int kRG = 16;      // gate/up rows per block (4 when T == 1)
+constexpr int kRD = 64;      // down rows per block (32 when T == 1)
 constexpr int kRDMin = 32;   // smallest down slice: bounds the number of slice tickets
-// weight pieces per lane held in registers (gate/up: per matrix), by tokens per batch
-template <int NT> constexpr int kMaxPcG = NT == 1 ? 4 : MOE_PCG_MULTI;
-template <int NT> constexpr int kMaxPcD = NT == 1 ? 8 : MOE_PCD_MULTI;
+constexpr int kMaxPcG = 4;   // gate/up weight pieces per lane held in registers, per matrix
+constexpr int kMaxPcD = 8;   // down weight pieces per lane held in registers
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
@@ -144,7 +133,7 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
   const float tsg = tensor_scale<FMT>(G, e), tsu = tensor_scale<FMT>(U, e);
   // When every piece fits in registers they are loaded once, before the
   // tokens are staged, so both memory latencies overlap.
-  constexpr int PC = kMaxPcG<NT>;
+  constexpr int PC = kMaxPcG;
   const bool resident = npc <= PC;
   RawPiece rg[PC], ru[PC];
   const int row0 = i0 + wave * rpw + rsub;
@@ -211,7 +200,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   uint16_t* xs = (uint16_t*)smem;
   float* xsum = (float*)(smem + (size_t)NT * K * sizeof(uint16_t));
   const float ts = tensor_scale<FMT>(D, e);
-  constexpr int PC = kMaxPcD<NT>;
+  constexpr int PC = kMaxPcD;
   const bool resident = npc <= PC;  // every piece stays in registers across token batches
   const int row0 = n0 + wave * rpw + rsub;
   RawPiece rd[PC];
@@ -753,12 +742,9 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   // a single token has little work per block: smaller slices spread it over more CUs
   a.rg = T == 1 ? 4 : kRG;
   a.rd = T == 1 ? kRDMin : kRD;
-#ifndef MOE_RGS
-#define MOE_RGS 4
-#endif
   // The shared expert's blocks carry a whole token batch each: thin row
   // slices spread that work over more CUs while the router runs.
-  a.rgs = T == 1 ? 4 : MOE_RGS;
+  a.rgs = 4;
   a.ss_r = L->shared ? (a.Is + a.rgs - 1) / a.rgs : 0;
   a.slices_r = (a.I + a.rg - 1) / a.rg;
   a.slices_d = (a.H + a.rd - 1) / a.rd;

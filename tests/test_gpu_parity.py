@@ -567,9 +567,13 @@ def test_prefill_4096_zipf_sampled():
     assert err <= TOL_LAYER
 
 
-def test_layer_decode_large_batch_uses_grouped_gemm():
-    print("layer T=200 composed", flush=True)
-    layer = synth.make_layer(2, 2048, 768, 256, 6, 110, DEV)
-    x = synth.make_tokens(200, 2048, 110, DEV)
-    y, ids, w = run_layer(layer, x, x, 200)
-    check_layer(layer, x, x, y, ids, w, tokens=[0, 57, 123, 199])
+@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100)])
+def test_layer_decode_large_batch_uses_grouped_gemm(fmt, T):
+    """Above 64 tokens the layer is composed from the separate calls; 70 tokens
+    (420 pairs, under two per expert) take the GEMV grouped FFN, 100 and 200
+    the matrix-core one."""
+    print("layer composed", fmt, T, flush=True)
+    layer = synth.make_layer(fmt, 2048, 768, 256, 6, 110 + T, DEV)
+    x = synth.make_tokens(T, 2048, 110 + T, DEV)
+    y, ids, w = run_layer(layer, x, x, T)
+    check_layer(layer, x, x, y, ids, w, tokens=[0, T // 3, (2 * T) // 3, T - 1])

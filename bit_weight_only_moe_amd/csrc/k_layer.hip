@@ -59,6 +59,7 @@ constexpr int kRDMin = 32;   // smallest down slice: bounds the number of slice 
 // the reductions of a whole wave per row (measured, 4 to 64 tokens: 9 to 17%
 // faster layer calls; 8 lanes is slower).
 constexpr int kLprTokens = 16;
+constexpr int kLprDownTokens = 4;  // the same for down rows (I = 768: 2% faster at 64 tokens than 8)
 constexpr int kMaxPcG = 4;   // gate/up weight pieces per lane held in registers, per matrix
 constexpr int kMaxPcD = 8;   // down weight pieces per lane held in registers
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
@@ -680,7 +681,7 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   g.slices_r = (I + kRG - 1) / kRG;
   g.slices_d = (H + kRD - 1) / kRD;
   g.lpr_h = std::min(lanes_per_row(H), kLprTokens);
-  g.lpr_i = lanes_per_row(I);
+  g.lpr_i = std::min(lanes_per_row(I), kLprDownTokens);
   constexpr int NT = 8;
   const size_t lds = std::max((size_t)NT * H * 2 + (size_t)NT * (H / 32) * 4,
                               (size_t)NT * I * 2 + (size_t)NT * (I / 32) * 4);
@@ -751,8 +752,8 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.slices_r = (a.I + a.rg - 1) / a.rg;
   a.slices_d = (a.H + a.rd - 1) / a.rd;
   a.lpr_h = std::min(lanes_per_row(a.H), NT == 1 ? 64 : kLprTokens);
-  a.lpr_i = lanes_per_row(a.I);
-  a.lpr_is = a.Is ? lanes_per_row(a.Is) : 64;
+  a.lpr_i = std::min(lanes_per_row(a.I), NT == 1 ? 64 : kLprDownTokens);
+  a.lpr_is = a.Is ? std::min(lanes_per_row(a.Is), NT == 1 ? 64 : kLprDownTokens) : 64;
   a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const bool nv = L->experts.gate.fmt == kFmtNvfp4;

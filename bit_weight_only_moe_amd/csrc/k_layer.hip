@@ -299,11 +299,12 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     __syncthreads();
     MOE_TRACE_AT(0, 1);
     if (e < E) {
-      float acc[kRouteT];
-      router_dots<kRouteT>(a.w_router + (size_t)e * H, (const uint16_t*)smem, H, nt, lane, acc, wv);
+      constexpr int RT = NT == 1 ? 1 : kRouteT;  // a lone token computes one chain
+      float acc[RT];
+      router_dots<RT>(a.w_router + (size_t)e * H, (const uint16_t*)smem, H, nt, lane, acc, wv);
       // device-coherent stores: the block that takes the batch's last ticket reads them
 #pragma unroll
-      for (int t = 0; t < kRouteT; ++t)
+      for (int t = 0; t < RT; ++t)
         if (t < nt && lane == 63) st_dev(a.logits + (size_t)(t0 + t) * E + e, acc[t]);
     }
   }

@@ -26,6 +26,10 @@ MOE_DEV void router_prefetch(const float* __restrict__ wrow, int H, int lane, fl
   }
 }
 
+// acc[t] = wrow . x_t for the nt <= RT tokens staged at xs (bf16, row t at
+// xs + t*H), reduced over the wave.  The tokens are the inner loop and every
+// token slot is computed (slots past nt read zeros), so the RT accumulation
+// chains interleave instead of running one after another.
 template <int RT>
 MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restrict__ xs, int H, int nt, int lane,
                          float (&acc)[RT], float4 (&wv)[kRouterC]) {
@@ -43,20 +47,20 @@ MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restr
       }
     }
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if (t < nt) {
+    for (int q = 0; q < kRouterC; ++q) {
+      const int c = cb + lane + 64 * q;
+      if (c < nc) {
+        uint2 v[RT];
 #pragma unroll
-        for (int q = 0; q < kRouterC; ++q) {
-          const int c = cb + lane + 64 * q;
-          if (c < nc) {
-            const uint2 v = xv2[t * nc + c];
-            float a = acc[t];
-            a = fmaf(wv[q].x, bf16_to_f32(v.x & 0xffffu), a);
-            a = fmaf(wv[q].y, bf16_to_f32(v.x >> 16), a);
-            a = fmaf(wv[q].z, bf16_to_f32(v.y & 0xffffu), a);
-            a = fmaf(wv[q].w, bf16_to_f32(v.y >> 16), a);
-            acc[t] = a;
-          }
+        for (int t = 0; t < RT; ++t) v[t] = t < nt ? xv2[t * nc + c] : make_uint2(0u, 0u);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          float a = acc[t];
+          a = fmaf(wv[q].x, __uint_as_float(v[t].x << 16), a);
+          a = fmaf(wv[q].y, __uint_as_float(v[t].x & 0xffff0000u), a);
+          a = fmaf(wv[q].z, __uint_as_float(v[t].y << 16), a);
+          a = fmaf(wv[q].w, __uint_as_float(v[t].y & 0xffff0000u), a);
+          acc[t] = a;
         }
       }
     }

@@ -64,9 +64,10 @@ MOE_DEV bool tile_of(const MfmaArgs& g, int mt, int& e, int& r0, int& r1) {
   return true;
 }
 
-// Tile tables, one block: each expert's rows in 128-row tiles (`big`); with
-// `split`, a final remainder of 1..64 rows becomes one 64-row tile (`small`)
-// instead.  Each table: [0] = count, then (expert, first row) pairs.
+// Tile tables, one block (one thread per expert, E <= 1024): each expert's
+// rows in tiles of bm rows (`big`); with `split` (bm = 128), a final remainder
+// of 1..64 rows becomes one 64-row tile (`small`) instead.  Each table: [0] =
+// count, then (expert, first row) pairs.
 __global__ void __launch_bounds__(1024) k_tile_table(const int32_t* __restrict__ offsets, int E, int rows, int bm,
                                                      int split, int32_t* __restrict__ big, int32_t* __restrict__ small) {
   __shared__ int scan_lds[17];

@@ -9,8 +9,8 @@
 //                   h = bf16(silu(G) * U);
 //   down kernel:    O = h_e Wd_e^T over K = I, fp32.
 // A device-side table lists (expert, first row) for every row tile.
-// Main path (k_mfma_bd): 64-row tiles; each lane streams its own weight
-// column from HBM into registers and dequantises it there.  With Zipf-skewed
+// Main path (k_mfma_bl for NVFP4, k_mfma_bd for INT4): 64-row tiles; each
+// lane dequantises its own weight column in registers.  With Zipf-skewed
 // routing most experts get a few dozen rows, so small tiles waste little
 // matrix work on padding.  Other shapes: 128-row tiles with the weights
 // dequantised into LDS, and an expert's final remainder of at most 64 rows
@@ -399,22 +399,25 @@ __global__ void __launch_bounds__(256, (WM == 1 && FMT == kFmtNvfp4) ? 3 : 2) k_
   }
 }
 
-// ------------------------------------------------------------------ weights straight into registers
+// ------------------------------------------------------------------ 64-row tiles, streamed weights
 // Block: 4 waves side by side over the columns, each covering all 32 * RF
-// rows of the tile.  Lane l streams the packed codes of its own B column
-// (l % 32) from HBM into registers ahead of their use, dequantises them there
-// and hands them to the matrix core as the B operand: the weights never pass
-// through LDS and need no barrier.  Only the activations, which the 4 waves
-// share, are staged in LDS (two buffers, one barrier per K step).
-// K order inside a 64-wide step (one INT4 group): matrix slice ks takes
-// k = ks*8 .. +8 from lane half 0 and k = 32 + ks*8 .. +8 from lane half 1,
-// so a lane's 32 weights of a step are one contiguous 16-byte run of codes;
-// the activation fragments are read from LDS in the same order.  Both
-// halves of a slice lie in the same INT4 group.
-// NVFP4 loads the codes and block scales of 4 K steps at once (ring of two
-// such groups): the 4 x 32 bytes a row gives in those steps are one 128-byte
-// line, requested together.  INT4 keeps a ring of 4 single steps (its group
-// partial sums leave no registers for more).
+// rows of the tile; only HBM-sized state is per block, so two blocks share a
+// CU.  Each lane dequantises the packed codes of its own B column (l % 32)
+// in registers and hands them to the matrix core as the B operand; the
+// activations, which the 4 waves share, go through LDS (two buffers, one
+// barrier per K step).
+// K order inside a 64-wide step (one INT4 group, four NVFP4 blocks): matrix
+// slice ks takes k = ks*8 .. +8 from lane half 0 and k = 32 + ks*8 .. +8 from
+// lane half 1, so a lane's 32 weights of a step are one contiguous 16-byte
+// run of codes; the activation fragments are read from LDS in the same order.
+// Both halves of a slice lie in the same INT4 group.
+// INT4 (k_mfma_bd): each lane loads its column's codes straight from HBM into
+// registers, a ring of 4 single steps (its group partial sums leave no
+// registers for more).
+// NVFP4 (k_mfma_bl): the codes of 4 K steps (one 128-byte line per weight
+// row) are loaded cooperatively, 8 lanes per row, into a double-buffered LDS
+// tile, from which each lane reads its column's 16 bytes per step; the block
+// scales of those 4 steps are one 16-byte load per lane.
 // GU: column pair cf = 0 / 1 is gate / up feature f = n0 + wave*32 + l%32
 //     (the block covers 128 features); h = bf16(silu(G) * U).
 // !GU: columns n0 + wave*64 + cf*32 + l%32 (the block covers 256 outputs).
@@ -446,7 +449,7 @@ static inline bool bd_k_ok(int fmt, int K) {
 
 template <int FMT, int RF, bool GU>
 __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
-  constexpr bool NV = FMT == kFmtNvfp4;
+  static_assert(FMT == kFmtInt4, "INT4 only (NVFP4: k_mfma_bl)");
   constexpr int BM = 32 * RF, D = 4, NB = GU ? 128 : 256;
   constexpr int AV = BM / 32;       // activation uint4 per thread per K step
   __shared__ uint4 As[2][BM * 8];   // [BM][64] bf16, swizzled, two buffers
@@ -484,21 +487,13 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
     const uint8_t* scales = GU ? (cf ? g.us : g.gs) : g.ds;
     const uint8_t* zeros = GU ? (cf ? g.uz : g.gz) : g.dz;
     bcp[cf] = codes + row * (K / 2) + hf * 16;
-    if (NV) {
-      bsp[cf] = scales + row * (K / 16);  // both halves' scales: 16 bytes per 4 steps
-      bzp[cf] = nullptr;
-    } else {
-      bsp[cf] = scales + row * (K / 64) * 2;
-      bzp[cf] = zeros + row * (K / 64);
-    }
+    bsp[cf] = scales + row * (K / 64) * 2;
+    bzp[cf] = zeros + row * (K / 64);
   }
   // Plain vectors, not uint4: a struct copy from global memory becomes a
   // block copy through private memory.  Activations: ring of D steps.
   u32x4_t ar[AV][D];
-  // NVFP4 weights: two groups of 4 steps (codes, 16 scale bytes per column)
-  u32x4_t gq[2][4][2];
-  u32x4_t gsv[2][2];
-  // INT4 weights: ring of D steps
+  // weights: ring of D steps
   u32x4_t bq[D][2];
   int bz[D][2];
   float bgs[D][2];
@@ -506,15 +501,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
 #pragma unroll
     for (int v = 0; v < AV; ++v) ar[v][j] = asrc[v][kt * 8];
   };
-  auto load_group = [&](int kt0, int grp) __attribute__((always_inline)) {  // NVFP4, steps kt0 .. kt0 + 3
-#pragma unroll
-    for (int cf = 0; cf < 2; ++cf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gq[grp][j][cf] = *(const u32x4_t*)(bcp[cf] + (kt0 + j) * 32);
-      gsv[grp][cf] = *(const u32x4_t*)(bsp[cf] + kt0 * 4);
-    }
-  };
-  auto load_b = [&](int kt, int j) __attribute__((always_inline)) {  // INT4, one step
+  auto load_b = [&](int kt, int j) __attribute__((always_inline)) {  // one step
 #pragma unroll
     for (int cf = 0; cf < 2; ++cf) {
       bq[j][cf] = *(const u32x4_t*)(bcp[cf] + kt * 32);
@@ -536,44 +523,25 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   const int nk = K / kBK;
   // loads past the last K step repeat it (in bounds, never used)
   load_a(0, 0);
-  if (NV) {
-    load_group(0, 0);
-    if (4 < nk) load_group(4, 1);
-  } else {
-    load_b(0, 0);
-  }
+  load_b(0, 0);
   load_a(min(1, nk - 1), 1);
-  if (!NV) load_b(min(1, nk - 1), 1);
+  load_b(min(1, nk - 1), 1);
   load_a(min(2, nk - 1), 2);
-  if (!NV) load_b(min(2, nk - 1), 2);
+  load_b(min(2, nk - 1), 2);
   load_a(min(3, nk - 1), 3);
-  if (!NV) load_b(min(3, nk - 1), 3);
+  load_b(min(3, nk - 1), 3);
   write_a(0, 0);
   __syncthreads();
   MOE_TRACE_BD(GU ? 0 : 1, 1);
   auto step = [&](auto kc) __attribute__((always_inline)) {
-    constexpr int kt = decltype(kc)::value, j = kt % D, grp = (kt / 4) & 1;
+    constexpr int kt = decltype(kc)::value, j = kt % D;
     write_a((j + 1) % D, (kt + 1) & 1);  // after the last step: unused
     uint4 o[2][4];
-    float s0 = 1.f, s1 = 1.f;
-    if (NV) {
-#pragma unroll
-      for (int cf = 0; cf < 2; ++cf) {
-        const uint32_t sc = gsv[grp][cf][j] >> (16 * hf);  // this half's two block scales
-        dequant32<FMT>(to_uint4(gq[grp][j][cf]), sc, 0, o[cf]);
-      }
-    } else {
-      dequant32<FMT>(to_uint4(bq[j][0]), 0, bz[j][0], o[0]);
-      dequant32<FMT>(to_uint4(bq[j][1]), 0, bz[j][1], o[1]);
-      s0 = bgs[j][0];
-      s1 = bgs[j][1];
-    }
+    dequant32<FMT>(to_uint4(bq[j][0]), 0, bz[j][0], o[0]);
+    dequant32<FMT>(to_uint4(bq[j][1]), 0, bz[j][1], o[1]);
+    const float s0 = bgs[j][0], s1 = bgs[j][1];
     load_a(min(kt + D, nk - 1), j);
-    if (NV) {
-      if (j == 0 && kt + 4 < nk && kt >= 4) load_group(kt + 4, grp ^ 1);
-    } else {
-      load_b(min(kt + D, nk - 1), j);
-    }
+    load_b(min(kt + D, nk - 1), j);
     const uint4* at = As[kt & 1];
     f32x16_t part[2][RF];
 #pragma unroll
@@ -589,23 +557,17 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
       for (int cf = 0; cf < 2; ++cf) {
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, o[cf][ks]);
 #pragma unroll
-        for (int rf = 0; rf < RF; ++rf) {
-          if (NV)
-            acc[cf][rf] = mfma(a[rf], b, acc[cf][rf]);
-          else
-            part[cf][rf] = mfma(a[rf], b, part[cf][rf]);
-        }
+        for (int rf = 0; rf < RF; ++rf) part[cf][rf] = mfma(a[rf], b, part[cf][rf]);
       }
     }
-    if (!NV) {
+    // each K step is one quantisation group: scale its partial sums in fp32
 #pragma unroll
-      for (int rf = 0; rf < RF; ++rf)
+    for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          acc[0][rf][i] = fmaf(s0, part[0][rf][i], acc[0][rf][i]);
-          acc[1][rf][i] = fmaf(s1, part[1][rf][i], acc[1][rf][i]);
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        acc[0][rf][i] = fmaf(s0, part[0][rf][i], acc[0][rf][i]);
+        acc[1][rf][i] = fmaf(s1, part[1][rf][i], acc[1][rf][i]);
+      }
     __syncthreads();
     if (kt == 0) MOE_TRACE_BD(GU ? 0 : 1, 2);
     if (kt == 3) MOE_TRACE_BD(GU ? 0 : 1, 3);
@@ -617,7 +579,152 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   unrolled_steps<0, kBdMaxSteps>(nk, step);
   MOE_TRACE_BD(GU ? 0 : 1, 6);
   if (GU) {
-    const float tsg = NV ? g.gts[e] : 1.f, tsu = NV ? g.uts[e] : 1.f;
+    const int f = n0 + wave * 32 + l32;
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = rf * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+        if (r0 + row < r1)
+          g.h[(size_t)(r0 + row) * N + f] = (uint16_t)f32_to_bf16_rne(silu_f32(acc[0][rf][i]) * acc[1][rf][i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+      const int col = n0 + wave * 64 + cf * 32 + l32;
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = rf * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+          if (r0 + row < r1) g.out[(size_t)(r0 + row) * N + col] = acc[cf][rf][i];
+        }
+      }
+    }
+  }
+}
+
+// NVFP4: the 256 weight rows of a block (gate + up features, or down
+// columns) are loaded 4 K steps (128 bytes of a row) at a time by 8
+// consecutive lanes, so one load instruction covers 8 whole cache lines
+// rather than 16-byte pieces of 32 (measured: 2-4% faster than per-lane
+// streaming into registers).  LDS: activations 2 x 8 KB, codes 2 x 32 KB.
+template <int FMT, bool GU>
+__global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
+  static_assert(FMT == kFmtNvfp4, "NVFP4 only");
+  constexpr int RF = 2, BM = 64, D = 4, NB = GU ? 128 : 256, AV = 2;
+  __shared__ uint4 As[2][BM * 8];
+  __shared__ uint4 Bs[2][256 * 8];  // [256 weight rows][128 bytes], chunk c at c ^ (row & 7)
+  const int K = GU ? g.H : g.I, N = GU ? g.I : g.H;
+  int tile, slice;
+  block_tile_chunked(N / NB, g.tiles[0], tile, slice);
+  int e, r0, r1;
+  if (!tile_of(g, tile, e, r0, r1)) return;
+  const int n0 = slice * NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int a_chunk = tid & 7;
+  const u32x4_t* asrc[AV];
+#pragma unroll
+  for (int v = 0; v < AV; ++v) {
+    const int arow = min(r0 + v * 32 + (tid >> 3), r1 - 1);
+    if (GU) {
+      const int tok = g.sorted_pairs ? g.sorted_pairs[arow] / g.k : arow;
+      asrc[v] = (const u32x4_t*)(g.x + (size_t)tok * K) + a_chunk;
+    } else {
+      asrc[v] = (const u32x4_t*)(g.h + (size_t)arow * K) + a_chunk;
+    }
+  }
+  // block weight row br: GU: gate feature br (br < 128) or up feature br - 128;
+  // down: output column br
+  auto brow_codes = [&](int br) __attribute__((always_inline)) {
+    if (GU) return (br < 128 ? g.gc : g.uc) + ((size_t)e * N + n0 + (br & 127)) * (K / 2);
+    return g.dc + ((size_t)e * N + n0 + br) * (K / 2);
+  };
+  // this thread's 8 group loads: rows i*32 + tid/8, 16-byte chunk tid % 8
+  const uint8_t* gsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gsrc[i] = brow_codes(i * 32 + (tid >> 3)) + a_chunk * 16;
+  // this lane's two B columns (rows of Bs) and their block scales
+  int lrow[2];
+  const uint8_t* bsp[2];
+#pragma unroll
+  for (int cf = 0; cf < 2; ++cf) {
+    lrow[cf] = GU ? cf * 128 + wave * 32 + l32 : wave * 64 + cf * 32 + l32;
+    const size_t row = GU ? (size_t)e * N + n0 + wave * 32 + l32 : (size_t)e * N + n0 + lrow[cf];
+    bsp[cf] = (GU ? (cf ? g.us : g.gs) : g.ds) + row * (K / 16);
+  }
+  u32x4_t ar[AV][D];
+  u32x4_t gr[8];        // next group's codes, in flight
+  u32x4_t gsv[2][2];    // block scales of the current and next group
+  auto load_a = [&](int kt, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) ar[v][j] = asrc[v][kt * 8];
+  };
+  auto write_a = [&](int j, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) ((u32x4_t*)As[buf])[swz(v * 32 + (tid >> 3), a_chunk)] = ar[v][j];
+  };
+  auto load_group = [&](int grp_step0, int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gr[i] = *(const u32x4_t*)(gsrc[i] + grp_step0 * 32);
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) gsv[sb][cf] = *(const u32x4_t*)(bsp[cf] + grp_step0 * 4);
+  };
+  auto write_group = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int br = i * 32 + (tid >> 3);
+      ((u32x4_t*)Bs[buf])[br * 8 + (a_chunk ^ (br & 7))] = gr[i];
+    }
+  };
+  f32x16_t acc[2][RF];
+#pragma unroll
+  for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) acc[cf][rf] = f32x16_t{};
+  const int nk = K / kBK;
+  load_group(0, 0);
+  load_a(0, 0);
+  load_a(min(1, nk - 1), 1);
+  load_a(min(2, nk - 1), 2);
+  load_a(min(3, nk - 1), 3);
+  write_group(0);
+  write_a(0, 0);
+  __syncthreads();
+  auto step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int kt = decltype(kc)::value, j = kt % D, grp = (kt / 4) & 1;
+    write_a((j + 1) % D, (kt + 1) & 1);  // after the last step: unused
+    uint4 o[2][4];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+      const int br = lrow[cf], c = 2 * j + hf;
+      const uint4 codes = Bs[grp][br * 8 + (c ^ (br & 7))];
+      const uint32_t sc = gsv[grp][cf][j] >> (16 * hf);
+      dequant32<FMT>(codes, sc, 0, o[cf]);
+    }
+    load_a(min(kt + D, nk - 1), j);
+    const bool more = kt + 4 < nk;
+    if (j == 0 && more) load_group(kt + 4, grp ^ 1);
+    const uint4* at = As[kt & 1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t a[RF];
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf) a[rf] = lds_frag(at, rf * 32 + l32, hf * 4 + ks);
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, o[cf][ks]);
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf) acc[cf][rf] = mfma(a[rf], b, acc[cf][rf]);
+      }
+    }
+    if (j == 3 && more) write_group(grp ^ 1);  // the other buffer's last reader was step kt - 3
+    __syncthreads();
+  };
+  unrolled_steps<0, kBdMaxSteps>(nk, step);
+  if (GU) {
+    const float tsg = g.gts[e], tsu = g.uts[e];
     const int f = n0 + wave * 32 + l32;
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf) {
@@ -631,10 +738,10 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
       }
     }
   } else {
-    const float ts = NV ? g.dts[e] : 1.f;
+    const float ts = g.dts[e];
 #pragma unroll
     for (int cf = 0; cf < 2; ++cf) {
-      const int col = n0 + wave * 64 + cf * 32 + l32;
+      const int col = n0 + lrow[cf];
 #pragma unroll
       for (int rf = 0; rf < RF; ++rf) {
 #pragma unroll
@@ -823,7 +930,7 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.dts = w->down.tensor_scale;
   g.h = h;
   g.out = out;
-  // Weights streamed into registers (k_mfma_bd): every tile is 64 rows.
+  // 64-row tiles everywhere (k_mfma_bl / k_mfma_bd).
   if (split && bd_k_ok(w->gate.fmt, H) && bd_k_ok(w->gate.fmt, I)) {
     hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, 64, 0, big, small);
     const unsigned b8 = (unsigned)((max_big + 7) / 8 * 8);
@@ -831,8 +938,8 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
     ga.tiles = big;
     ga.tile_rows = 64;
     if (w->gate.fmt == kFmtNvfp4) {
-      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
-      hipLaunchKernelGGL((k_mfma_bd<kFmtNvfp4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
+      hipLaunchKernelGGL((k_mfma_bl<kFmtNvfp4, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
+      hipLaunchKernelGGL((k_mfma_bl<kFmtNvfp4, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
     } else {
       hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
       hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);

@@ -24,7 +24,8 @@
 //             batch, row slice of H) per block, fp32 outputs to the
 //             workspace; the last block of each slice combines
 //             y = residual + sum_j w_j o_j + o_shared in that fixed order and
-//             rounds to bf16.
+//             rounds to bf16.  A lone token instead: each block takes a few
+//             output rows of every unit and combines them in LDS itself.
 //
 // Every block loads all of its weight pieces before it uses any, so one
 // memory round trip covers a block's whole share of the expert bytes.
@@ -102,6 +103,7 @@ struct LayerArgs {
   int slices_d;              // down row slices of H
   int lpr_h, lpr_i, lpr_is;
   int down_stage_bytes;      // launch 3: LDS bytes of the token staging (16-byte multiple)
+  int rows_t1;               // one token: output rows per down block, every unit (0: not used)
 };
 
 
@@ -565,6 +567,116 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   MOE_TRACE_AT(2, 5);
 }
 
+// ------------------------------------------------------------------ launch 3, one token
+// A lone token meets each of its k experts and the shared expert once, so
+// one block takes rows [n0, n0 + R) of every unit: R * units row-dots, one
+// per lane group, in a single pass.  The outputs meet in LDS and the block
+// writes y for its rows itself, so no slice ticket and no reload of the
+// other units' outputs.  Each row-dot uses the lanes, pieces and reduction
+// of down_rows, and the combine takes the same order as the multi-block
+// combine: the results are those of the general launch 3, bit for bit.
+constexpr int kMaxUnitsT1 = 9;   // k <= 8 routed experts + the shared expert
+#ifndef MOE_T1_THREADS
+#define MOE_T1_THREADS 256
+#endif
+constexpr int kT1Threads = MOE_T1_THREADS;
+template <int FMT>
+__global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_e[kMaxUnitsT1];
+  __shared__ float s_w[kMaxUnitsT1];
+  __shared__ int s_pp[kMaxUnitsT1];
+  __shared__ float s_o[kT1Threads];  // [unit][row]: units * R <= lane groups <= threads
+  MOE_TRACE_AT(2, 0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int H = a.H, I = a.I, k = a.k, R = a.rows_t1;
+  const bool has_shared = a.nsb > 0;
+  const int nu = k + (has_shared ? 1 : 0);
+  const int n0 = blockIdx.x * R;
+  // record r holds the expert of rank r, whose h row is r (written by launch 1)
+  if (tid < k) {
+    s_e[tid] = a.rec[(size_t)tid * kRec];
+    s_w[tid] = a.w[tid];
+    s_pp[tid] = a.pair_pos[tid];
+  } else if (tid < kMaxUnitsT1) {  // padding read by the combine, never used
+    s_w[tid] = 0.f;
+    s_pp[tid] = 0;
+  }
+  __syncthreads();
+  MOE_TRACE_AT(2, 1);
+  const int lpr = a.lpr_i, rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
+  const int ppl = (I / 32) / lpr;
+  const int d = wave * rpw + rsub;  // this lane group's row-dot: unit d / R, row n0 + d % R
+  const int u = d / R, n = n0 + d % R;
+  const bool active = u < nu && n < H;
+  // idle lane groups load a valid row too (results unused): no divergent
+  // branch among the loads
+  const int uc = min(u, nu - 1), nc = min(n, H - 1);
+  const bool sh = uc == k;
+  const MatDev& D = sh ? a.sdown : a.down;
+  const int e = sh ? 0 : s_e[uc];
+  // The h rows (unit t < k: routed row t; unit k: the shared row) go to LDS
+  // piece-transposed.  Their loads are issued before the weight loads, so the
+  // LDS stores wait for them alone.
+  uint16_t* xs = (uint16_t*)smem;                                  // nu rows of I
+  float* xsum = (float*)(smem + (size_t)nu * I * sizeof(uint16_t));  // INT4 piece sums
+  const int ppt = I / 32, total = nu * ppt;
+  auto h_piece = [&](int p) {
+    const int t = p / ppt;
+    return load_piece64((t < k ? a.h_routed + (size_t)t * I : a.h_shared) + 32 * (p - t * ppt));
+  };
+  Piece64 hv0, hv1;
+  const int hp0 = tid, hp1 = tid + kT1Threads;
+  if (hp0 < total) hv0 = h_piece(hp0);
+  if (hp1 < total) hv1 = h_piece(hp1);
+  RawPiece rd[kMaxPcD];
+  {
+    const uint8_t* rc = row_codes(D, e, nc);
+    const uint8_t* rs = row_scales<FMT>(D, e, nc);
+    const uint8_t* rz = row_zeros(D, e, nc);
+#pragma unroll
+    for (int q = 0; q < kMaxPcD; ++q)
+      if (q < ppl) rd[q] = load_piece<FMT>(rc, rs, rz, lir + q * lpr);
+  }
+  auto h_store = [&](int p, const Piece64& v) {
+    const int t = p / ppt, c = p - t * ppt;
+    store_piece<FMT>((uint4*)(xs + (size_t)t * I) + c, ppt, xsum + p, v);
+  };
+  if (hp0 < total) h_store(hp0, hv0);
+  if (hp1 < total) h_store(hp1, hv1);
+  for (int p = tid + 2 * kT1Threads; p < total; p += kT1Threads) h_store(p, h_piece(p));
+  __syncthreads();
+  MOE_TRACE_AT(2, 2);
+  float acc[1] = {0.f};
+#pragma unroll
+  for (int q = 0; q < kMaxPcD; ++q)
+    if (q < ppl) piece_dot<FMT, 1>(rd[q], lir + q * lpr, xs + (size_t)uc * I, I, xsum + uc * (I / 32), I / 32, 1, acc);
+  acc[0] = group_sum_last_dyn(acc[0], lpr);
+  if (active && lir == lpr - 1) s_o[d] = acc[0] * tensor_scale<FMT>(D, e);
+  __syncthreads();
+  MOE_TRACE_AT(2, 3);
+  if (tid < R && n0 + tid < H) {
+    const int c = n0 + tid;
+    // every LDS read issued before the first use (a chain of dependent
+    // reads would cost one LDS round trip per choice)
+    float ow[kMaxUnitsT1 - 1], oo[kMaxUnitsT1 - 1];
+#pragma unroll
+    for (int j = 0; j < kMaxUnitsT1 - 1; ++j) {
+      ow[j] = s_w[j];
+      oo[j] = s_o[s_pp[j] * R + tid];
+    }
+    const float os = has_shared ? s_o[k * R + tid] : 0.f;
+    float acc2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxUnitsT1 - 1; ++j)
+      if (j < k) acc2 = fmaf(ow[j], oo[j], acc2);
+    if (has_shared) acc2 += os;
+    if (a.residual) acc2 += bf16_to_f32(a.residual[c]);
+    a.y[c] = (uint16_t)f32_to_bf16_rne(acc2);
+  }
+  MOE_TRACE_AT(2, 4);
+}
+
 // ------------------------------------------------------------------ grouped FFN (composed path)
 struct GroupedArgs {
   int H, I, k;
@@ -696,10 +808,30 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   return hipGetLastError();
 }
 
+// Rows per block of the single-token down launch, or 0 where the general
+// launch 3 is used: the shared expert (if any) must have the routed inter
+// size (its h row shares the staging layout), every unit's row-dots must fit
+// one pass of the block's lane groups, and a lane's pieces its registers.
+static int down_t1_rows(int T, int I, int Is, int k, bool shared) {
+  if (T != 1 || (shared && Is != I) || k > 8) return 0;
+  const int lpr = std::min(lanes_per_row(I), 64);
+  if ((I / 32) / lpr > kMaxPcD) return 0;
+  const int units = k + (shared ? 1 : 0);
+  const int rows = (kT1Threads / lpr) / units;
+  if (rows < 1 || (size_t)units * I * 2 + (size_t)units * (I / 32) * 4 > 64 * 1024) return 0;
+  return rows;
+}
+
 template <int FMT, int NT>
 static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
   hipLaunchKernelGGL((k_layer_route_shared<FMT, NT>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s, a);
   hipLaunchKernelGGL((k_layer_gateup<FMT, NT>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
+  if (NT == 1 && a.rows_t1 > 0) {
+    const int units = a.k + (a.nsb > 0 ? 1 : 0);
+    const size_t l1 = (size_t)units * a.I * 2 + (size_t)units * (a.I / 32) * 4;
+    hipLaunchKernelGGL((k_layer_down_t1<FMT>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s, a);
+    return;
+  }
   hipLaunchKernelGGL((k_layer_down_combine<FMT, NT>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256), lds.down,
                      s, a);
 }
@@ -756,6 +888,7 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.lpr_i = std::min(lanes_per_row(a.I), NT == 1 ? 64 : kLprDownTokens);
   a.lpr_is = a.Is ? std::min(lanes_per_row(a.Is), NT == 1 ? 64 : kLprDownTokens) : 64;
   a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
+  a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr);
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const bool nv = L->experts.gate.fmt == kFmtNvfp4;
   if (NT == 1)

@@ -35,9 +35,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # the factors that make the counters read 1 GiB each for a plain 1 GiB device copy
 # (profiles/hbm_traffic_counters.md).  Workloads not listed report null.
 TRAFFIC_BYTES = {
-    ("decode_b1", "nvfp4"): 21.93e6,
+    ("decode_b1", "nvfp4"): 21.76e6,
     ("decode_T16", "nvfp4"): 223.4e6,
-    ("prefill", "nvfp4"): 1250.6e6,
+    ("prefill", "nvfp4"): 1239.0e6,
 }
 
 
@@ -188,8 +188,9 @@ def main():
                    "distinct_experts_per_step": float(np.mean(touched))},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get((workload, args.fmt)),
-                     "kernel": "moe_layer_decode: k_layer_route_shared + k_layer_gateup + k_layer_down_combine "
-                               "(one layer call, events on the launch stream)",
+                     "kernel": "moe_layer_decode: k_layer_route_shared + k_layer_gateup + %s "
+                               "(one layer call, events on the launch stream)"
+                               % ("k_layer_down_t1" if T == 1 else "k_layer_down_combine"),
                      "bytes": "expert weights of the distinct touched experts + shared expert, per call"},
         "cpu_baseline": cpu,
     }
@@ -322,7 +323,8 @@ def bench_prefill(args, fmt):
         "roofline": {"bound": "mfma", "achieved": flops / (ms_ffn / K * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ms_ffn / K * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": TRAFFIC_BYTES.get(("prefill", args.fmt)),
-                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, k_mfma_bd gate/up, k_mfma_bd down"},
+                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, %s gate/up, %s down"
+                               % (("k_mfma_bl",) * 2 if fmt == 1 else ("k_mfma_bd",) * 2)},
         "cpu_baseline": None,
     }
     print(json.dumps(out_line))

@@ -346,6 +346,9 @@ LAYER_CASES = [
     ("flint_int4_T1", 2, 2048, 768, 256, 6, 1, 12, True),
     ("tiny_nvfp4_T1_k8", 1, 256, 128, 16, 8, 1, 13, True),
     ("tiny_int4_T1_k8", 2, 256, 128, 16, 8, 1, 14, False),
+    # one token, 7 units of 18 rows per down block: the last block is partial
+    ("ragged_H192_I320_T1", 1, 192, 320, 8, 6, 1, 15, True),
+    ("ragged_int4_H192_I320_T1", 2, 192, 320, 8, 6, 1, 16, False),
 ]
 
 

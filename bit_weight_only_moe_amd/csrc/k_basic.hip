@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restric
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
   float4 wv[kRouterC];
-  if (e < E) router_prefetch(wr + (size_t)e * H, H, lane, wv);
+  router_prefetch(wr + (size_t)min(e, E - 1) * H, H, lane, wv);  // past the last expert: unused
   copy_to_lds((uint4*)xs, (const uint4*)(x + (size_t)t0 * H), nt * H / 8);
   __syncthreads();
   if (e >= E) return;

@@ -296,7 +296,9 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   {
     const int e = (blockIdx.x % a.nRe) * 4 + wave;
     float4 wv[kRouterC];
-    if (e < E) router_prefetch(a.w_router + (size_t)e * H, H, lane, wv);
+    // a wave past the last expert loads the last expert's row (never used):
+    // no branch around the loads, whose registers the token copy then reuses
+    router_prefetch(a.w_router + (size_t)min(e, E - 1) * H, H, lane, wv);
     copy_to_lds((uint4*)smem, (const uint4*)(a.x + (size_t)t0 * H), nt * H / 8);
     __syncthreads();
     MOE_TRACE_AT(0, 1);

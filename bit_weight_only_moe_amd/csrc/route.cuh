@@ -16,20 +16,20 @@ constexpr int kRouterC = 8;  // float4 router loads in flight per lane
 
 // Load a wave's first kRouterC float4 of router row `wrow` (lane l takes
 // float4 l, l+64, ...): issued before the tokens are staged.
+// Chunks past the row's end load its last chunk instead (unconditional
+// loads: no zero-fill of a destination register between them); router_dots
+// never uses them.
 MOE_DEV void router_prefetch(const float* __restrict__ wrow, int H, int lane, float4 (&wv)[kRouterC]) {
   const float4* wr = (const float4*)wrow;
   const int nc = H / 4;
 #pragma unroll
-  for (int q = 0; q < kRouterC; ++q) {
-    const int c = lane + 64 * q;
-    wv[q] = c < nc ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int q = 0; q < kRouterC; ++q) wv[q] = wr[min(lane + 64 * q, nc - 1)];
 }
 
 // acc[t] = wrow . x_t for the nt <= RT tokens staged at xs (bf16, row t at
 // xs + t*H), reduced over the wave.  The tokens are the inner loop and every
-// token slot is computed (slots past nt read zeros), so the RT accumulation
-// chains interleave instead of running one after another.
+// token slot is computed, so the RT accumulation chains interleave instead
+// of running one after another.
 template <int RT>
 MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restrict__ xs, int H, int nt, int lane,
                          float (&acc)[RT], float4 (&wv)[kRouterC]) {
@@ -41,18 +41,17 @@ MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restr
   for (int cb = 0; cb < nc; cb += 64 * kRouterC) {
     if (cb > 0) {
 #pragma unroll
-      for (int q = 0; q < kRouterC; ++q) {
-        const int c = cb + lane + 64 * q;
-        wv[q] = c < nc ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int q = 0; q < kRouterC; ++q) wv[q] = wr[min(cb + lane + 64 * q, nc - 1)];
     }
 #pragma unroll
     for (int q = 0; q < kRouterC; ++q) {
       const int c = cb + lane + 64 * q;
       if (c < nc) {
+        // slots past nt read the last staged token (no branch between the
+        // LDS reads); their sums are never stored
         uint2 v[RT];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) v[t] = t < nt ? xv2[t * nc + c] : make_uint2(0u, 0u);
+        for (int t = 0; t < RT; ++t) v[t] = xv2[min(t, nt - 1) * nc + c];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           float a = acc[t];
@@ -70,32 +69,34 @@ MOE_DEV void router_dots(const float* __restrict__ wrow, const uint16_t* __restr
     if (t < nt) acc[t] = group_sum_last<64>(acc[t]);
 }
 
-// Copy n16 16-byte chunks from global to LDS, eight loads in flight per
-// thread before the stores (named registers, not an array, so nothing goes
-// through private memory).
+// Copy n16 16-byte chunks from global to LDS.  A thread's first eight
+// chunks are straight-line code with all loads issued before the stores, so
+// loads the caller issued just before (the router weights) stay in flight
+// with these (a loop header here would make the compiler wait for them
+// first); the rare remainder is a plain loop.  Named registers, not an
+// array, so nothing goes through private memory.
 MOE_DEV void copy_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16) {
-  const int nthr = blockDim.x;
-  for (int i0 = threadIdx.x; i0 < n16; i0 += 8 * nthr) {
-    const int i1 = i0 + nthr, i2 = i0 + 2 * nthr, i3 = i0 + 3 * nthr;
-    const int i4 = i0 + 4 * nthr, i5 = i0 + 5 * nthr, i6 = i0 + 6 * nthr, i7 = i0 + 7 * nthr;
-    uint4 v0, v1, v2, v3, v4, v5, v6, v7;
-    v0 = src[i0];
-    if (i1 < n16) v1 = src[i1];
-    if (i2 < n16) v2 = src[i2];
-    if (i3 < n16) v3 = src[i3];
-    if (i4 < n16) v4 = src[i4];
-    if (i5 < n16) v5 = src[i5];
-    if (i6 < n16) v6 = src[i6];
-    if (i7 < n16) v7 = src[i7];
-    dst[i0] = v0;
-    if (i1 < n16) dst[i1] = v1;
-    if (i2 < n16) dst[i2] = v2;
-    if (i3 < n16) dst[i3] = v3;
-    if (i4 < n16) dst[i4] = v4;
-    if (i5 < n16) dst[i5] = v5;
-    if (i6 < n16) dst[i6] = v6;
-    if (i7 < n16) dst[i7] = v7;
-  }
+  const int nthr = blockDim.x, i0 = threadIdx.x;
+  const int i1 = i0 + nthr, i2 = i0 + 2 * nthr, i3 = i0 + 3 * nthr;
+  const int i4 = i0 + 4 * nthr, i5 = i0 + 5 * nthr, i6 = i0 + 6 * nthr, i7 = i0 + 7 * nthr;
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+  if (i0 < n16) v0 = src[i0];
+  if (i1 < n16) v1 = src[i1];
+  if (i2 < n16) v2 = src[i2];
+  if (i3 < n16) v3 = src[i3];
+  if (i4 < n16) v4 = src[i4];
+  if (i5 < n16) v5 = src[i5];
+  if (i6 < n16) v6 = src[i6];
+  if (i7 < n16) v7 = src[i7];
+  if (i0 < n16) dst[i0] = v0;
+  if (i1 < n16) dst[i1] = v1;
+  if (i2 < n16) dst[i2] = v2;
+  if (i3 < n16) dst[i3] = v3;
+  if (i4 < n16) dst[i4] = v4;
+  if (i5 < n16) dst[i5] = v5;
+  if (i6 < n16) dst[i6] = v6;
+  if (i7 < n16) dst[i7] = v7;
+  for (int i = i0 + 8 * nthr; i < n16; i += nthr) dst[i] = src[i];
 }
 
 // Copy n floats from global to LDS, eight loads in flight per thread.

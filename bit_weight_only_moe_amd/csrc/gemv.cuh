@@ -137,9 +137,14 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
     q[12] = e2m1x2_to_bf16<0>(c.w); q[13] = e2m1x2_to_bf16<1>(c.w);
     q[14] = e2m1x2_to_bf16<2>(c.w); q[15] = e2m1x2_to_bf16<3>(c.w);
   } else {
-    b0 = f16_to_f32((unsigned short)r.s);
+    // The scale and zero are converted here, at their use: left visible, the
+    // conversions are hoisted next to their loads and each piece's loads then
+    // wait for the previous piece's scale and zero before issuing.
+    uint32_t rs = r.s, rz = r.z;
+    asm volatile("" : "+v"(rs), "+v"(rz));
+    b0 = f16_to_f32((unsigned short)rs);
     b1 = 0.f;
-    zc = 128.0f + (float)r.z;
+    zc = 128.0f + (float)rz;
     q[0] = int4x2_to_bf16_off128<0>(c.x); q[1] = int4x2_to_bf16_off128<1>(c.x);
     q[2] = int4x2_to_bf16_off128<2>(c.x); q[3] = int4x2_to_bf16_off128<3>(c.x);
     q[4] = int4x2_to_bf16_off128<0>(c.y); q[5] = int4x2_to_bf16_off128<1>(c.y);

@@ -550,22 +550,58 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   }
   __syncthreads();
   const bool has_shared = a.nsb > 0;
-  const int rows = n1 - n0;
-  for (int idx = tid; idx < T * rows; idx += 256) {
-    const int t = idx / rows, c = n0 + idx % rows;
-    float o[8];
+  const int rows = n1 - n0, total = T * rows;
+  // U (token, column) outputs per thread and round, U = 1, 2 or 4 as the
+  // slice needs, all of their loads issued before the first sum: one memory
+  // round trip per round instead of one per output (this block is the
+  // launch's tail).  The loads are unconditional so that no branch splits
+  // them: outputs past the end re-read the last one, choices past k re-read
+  // choice k - 1, a missing shared expert or residual reads the routed
+  // outputs or the tokens instead; none of these enters a stored sum.
+  const float* osrc = has_shared ? a.o_shared : a.o_routed;
+  const uint16_t* rsrc = a.residual ? a.residual : a.x;
+  auto rounds = [&](auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    for (int base = tid; base < total; base += U * 256) {
+      float o[U][8], os[U];
+      uint32_t rsb[U];  // residual bits, converted at their use (converted here, the
+                        // shift would wait for every load issued so far)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = j < k ? a.o_routed[(size_t)s_pp[t * k + j] * H + c] : 0.f;
-    const float os = has_shared ? a.o_shared[(size_t)t * H + c] : 0.f;
-    const float rs = a.residual ? bf16_to_f32(a.residual[(size_t)t * H + c]) : 0.f;
-    float acc = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int idx = min(base + u * 256, total - 1);
+        const int t = idx / rows, c = n0 + idx % rows;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) acc = fmaf(s_w[t * k + j], o[j], acc);
-    if (has_shared) acc += os;
-    if (a.residual) acc += rs;
-    a.y[(size_t)t * H + c] = (uint16_t)f32_to_bf16_rne(acc);
-  }
+        for (int j = 0; j < 8; ++j) o[u][j] = a.o_routed[(size_t)s_pp[t * k + min(j, k - 1)] * H + c];
+        os[u] = osrc[(size_t)t * H + c];
+        rsb[u] = rsrc[(size_t)t * H + c];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = base + u * 256;
+        if (idx < total) {
+          const int t = idx / rows, c = n0 + idx % rows;
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j < k) acc = fmaf(s_w[t * k + j], o[u][j], acc);
+          if (has_shared) acc += os[u];
+          if (a.residual) {
+            uint32_t rb = rsb[u];
+            asm volatile("" : "+v"(rb));
+            acc += bf16_to_f32((uint16_t)rb);
+          }
+          a.y[(size_t)t * H + c] = (uint16_t)f32_to_bf16_rne(acc);
+        }
+      }
+    }
+  };
+  const int per_thread = (total + 255) / 256;
+  if (per_thread <= 1)
+    rounds(std::integral_constant<int, 1>{});
+  else if (per_thread <= 2)
+    rounds(std::integral_constant<int, 2>{});
+  else
+    rounds(std::integral_constant<int, 4>{});
   MOE_TRACE_AT(2, 5);
 }
 

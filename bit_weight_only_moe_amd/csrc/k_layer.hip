@@ -436,9 +436,12 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     loc += cnt[q];
     nz += cnt[q] > 0;
   }
-  int total, ntot;
-  int pre = block_exclusive_scan(loc, scan_tmp, total);
-  int apre = block_exclusive_scan(nz, scan_tmp, ntot);
+  // one scan for both prefix sums: pair counts in the low 16 bits (at most
+  // T*k <= 512 in all), touched experts in the high 16 bits (at most E)
+  int ptot;
+  const int pk = block_exclusive_scan(loc | (nz << 16), scan_tmp, ptot);
+  int pre = pk & 0xffff, apre = pk >> 16;
+  const int ntot = ptot >> 16;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int ee = tid * 4 + q;

@@ -431,10 +431,13 @@ def test_composed_calls_match_fused_layer():
     assert torch.equal(y.view(torch.int16), yf.view(torch.int16))
 
 
-def test_layer_decode_graph_capture_replays():
-    print("graph capture", flush=True)
-    H, I, E, k, T = 2048, 768, 256, 6, 4
-    layer = synth.make_layer(2, H, I, E, k, 90, DEV)
+@pytest.mark.parametrize("fmt,T", [(2, 4), (1, 1), (1, 16)])
+def test_layer_decode_graph_capture_replays(fmt, T):
+    """Replays of a captured layer call (the one-token path has its own down
+    launch; 16 tokens use several router batches) equal the eager call."""
+    print("graph capture", fmt, T, flush=True)
+    H, I, E, k = 2048, 768, 256, 6
+    layer = synth.make_layer(fmt, H, I, E, k, 90 + T, DEV)
     x = synth.make_tokens(T, H, 90, DEV)
     L = moe.Layer(layer)
     nws = moe.moe_layer_decode_workspace_size(L, T)

@@ -290,26 +290,41 @@ def bench_prefill(args, fmt):
     f_routed = [moe.ffn_weights(l["experts"]) for l in layers]
     f_shared = [moe.ffn_weights(l["shared"]) for l in layers]
 
+    # The shared expert needs no routing: its grouped FFN runs on a side stream
+    # (own workspace), alongside the router, top-k and permute kernels, which
+    # leave most of the chip idle, and the routed FFN; both join before the
+    # combine.
+    side = torch.cuda.Stream()
+    gws_s = torch.empty(gws_n, dtype=torch.uint8, device=dev)
+
+    def shared_ffn(i, s):
+        side.wait_stream(s)
+        moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws_s,
+                                  gws_n, stream=side)
+
+    def routed_ffn(i, s):
+        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
+                                  gws_n, stream=s)
+
     def step(i, s):
         L = layers[i % R]
+        shared_ffn(i, s)
         moe.moe_route(x, L["w_router"], T, H, E, k, lg, ids, w, stream=s)   # router GEMM (timed; skewed logits route)
         moe.moe_topk_softmax(zl, T, E, k, ids, w, stream=s)
         moe.moe_permute(ids, T, k, E, counts, offsets, sp, pp, None, None, 0, pws, pws_n, stream=s)
-        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
-                                  gws_n, stream=s)
-        moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws,
-                                  gws_n, stream=s)
+        routed_ffn(i, s)
+        s.wait_stream(side)
         moe.moe_combine(out, pp, w, out_s, x, T, k, H, y, stream=s)
+
+    def ffn_pair(i, s):
+        shared_ffn(i, s)
+        routed_ffn(i, s)
+        s.wait_stream(side)
 
     stream = torch.cuda.Stream()
     ms = timed_graph(torch, stream, step, K, W, not args.no_graph)
     # the grouped FFN alone (routed + shared), timed the same way
-    def ffn_only(i, s):
-        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
-                                  gws_n, stream=s)
-        moe.moe_grouped_w4a16_ffn(f_shared[i % R], 1, H, I, x, None, 1, off_s, T, out_s, moe.MOE_MODE_AUTO, gws,
-                                  gws_n, stream=s)
-    ms_ffn = timed_graph(torch, stream, ffn_only, K, W, not args.no_graph)
+    ms_ffn = timed_graph(torch, stream, ffn_pair, K, W, not args.no_graph)
     flops = 6.0 * (n + T) * H * I
     c = counts.cpu().numpy()
     out_line = {

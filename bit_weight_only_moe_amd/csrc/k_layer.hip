@@ -442,19 +442,19 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   const int pk = block_exclusive_scan(loc | (nz << 16), scan_tmp, ptot);
   int pre = pk & 0xffff, apre = pk >> 16;
   const int ntot = ptot >> 16;
+  int32_t* ridx = (int32_t*)s_log;  // [E] record index of each touched expert (the logits are done with)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int ee = tid * 4 + q;
     if (ee < E) {
       off[ee] = pre;
       if (cnt[q] > 0) {
+        ridx[ee] = apre;
         int32_t* r = a.rec + (size_t)(apre++) * kRec;
         r[0] = ee;
         r[1] = pre;
         r[2] = cnt[q];
         r[3] = 0;
-        unsigned long long m = mask[ee];
-        for (int i = 0; m; ++i, m &= m - 1ull) r[4 + i] = __builtin_ctzll(m);
       }
       pre += cnt[q];
     }
@@ -462,9 +462,13 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   for (int u = ntot + tid; u < a.max_active; u += 256) a.rec[(size_t)u * kRec] = -1;
   if (tid == 0) a.n_active[0] = ntot;
   __syncthreads();
+  // one thread per pair: its rank among its expert's tokens gives both its
+  // grouped row and its slot in the expert's record token list
   for (int p = tid; p < n; p += 256) {
     const int t = p / k, ee = s_ids[p];
-    a.pair_pos[p] = off[ee] + __popcll(mask[ee] & ((1ull << t) - 1ull));
+    const int rank = __popcll(mask[ee] & ((1ull << t) - 1ull));
+    a.pair_pos[p] = off[ee] + rank;
+    a.rec[(size_t)ridx[ee] * kRec + 4 + rank] = t;
     if (nb == 1) {
       a.ids[p] = ee;
       a.w[p] = s_w[p];

@@ -420,20 +420,16 @@ MOE_DEV int block_exclusive_scan(int v, int* lds, int& total) {
   const int inc = wave_inclusive_scan(v);
   if (lane == 63) lds[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int t = lds[w];
-      lds[w] = run;
-      run += t;
-    }
-    lds[16] = run;
+  // every thread sums the wave totals itself (at most 16): no serial pass
+  int before = 0, all = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const int t = lds[w];
+    before += w < wave ? t : 0;
+    all += t;
   }
-  __syncthreads();
-  const int res = lds[wave] + inc - v;
-  total = lds[16];
-  __syncthreads();
-  return res;
+  total = all;
+  __syncthreads();  // the caller may reuse lds
+  return before + inc - v;
 }
 
 }  // namespace moe

@@ -35,8 +35,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # the factors that make the counters read 1 GiB each for a plain 1 GiB device copy
 # (profiles/hbm_traffic_counters.md).  Workloads not listed report null.
 TRAFFIC_BYTES = {
-    ("decode_b1", "nvfp4"): 21.74e6,
-    ("decode_T16", "nvfp4"): 223.5e6,
+    ("decode_b1", "nvfp4"): 21.75e6,
+    ("decode_T16", "nvfp4"): 223.4e6,
     ("prefill", "nvfp4"): 1239.0e6,
 }
 

@@ -167,7 +167,10 @@ int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* top
 /* Whole layer for decode-sized batches (1 <= T <= 64 takes the fused path;
  * larger T is composed from the calls above): router, top-k, routed and
  * shared SwiGLU experts on 4-bit weights, combine.  Same numerics as
- * composing moe_route, moe_permute, moe_grouped_w4a16_ffn and moe_combine.
+ * composing moe_route, moe_permute, moe_grouped_w4a16_ffn and moe_combine;
+ * for 2 <= T <= 64 the result equals that composition (GEMV mode) bit for
+ * bit, while a lone token splits its dot products over more lanes (same
+ * contract, possibly different last bits).
  * residual bf16 [T, H] may be NULL; y bf16 [T, H]; ids_out int32 [T, k] and
  * w_out fp32 [T, k] may be NULL.  Workspace: moe_layer_decode_workspace_size
  * bytes, 256-byte aligned, ZERO-FILLED before its first use: its first

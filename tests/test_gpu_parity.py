@@ -397,12 +397,14 @@ def test_layer_decode_deterministic_and_token_independent():
     assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b)
 
 
-def test_composed_calls_match_fused_layer():
-    """route -> permute -> grouped FFN (routed, shared) -> combine equals moe_layer_decode."""
-    print("composed vs fused", flush=True)
-    H, I, E, k, T = 2048, 768, 256, 6, 6
-    layer = synth.make_layer(1, H, I, E, k, 80, DEV)
-    x = synth.make_tokens(T, H, 80, DEV)
+@pytest.mark.parametrize("fmt,T", [(1, 2), (1, 6), (2, 16), (1, 64)])
+def test_composed_calls_match_fused_layer(fmt, T):
+    """route -> permute -> grouped FFN (routed, shared; GEMV mode) -> combine
+    equals moe_layer_decode bit for bit for 2 <= T <= 64."""
+    print("composed vs fused", fmt, T, flush=True)
+    H, I, E, k = 2048, 768, 256, 6
+    layer = synth.make_layer(fmt, H, I, E, k, 80 + T, DEV)
+    x = synth.make_tokens(T, H, 80 + T, DEV)
     yf, idf, wf = run_layer(layer, x, x, T)
     lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
     ids = torch.empty((T, k), dtype=torch.int32, device=DEV)

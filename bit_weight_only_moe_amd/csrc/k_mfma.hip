@@ -756,13 +756,14 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
 
 // ------------------------------------------------------------------ router (large batches)
 // logits[t, e] = sum_h x[t, h] * w[e, h] on the matrix cores.  Each fp32
-// router weight is split exactly into three bf16 parts, w = hi + mid + lo
-// (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid, each residual exact
-// in fp32 and the last one exact in bf16), so every product x * part is exact
-// in fp32 and the three MFMAs accumulate them in fp32, as the VALU router's
-// fused multiply-adds do (in another order).  Block: 64 tokens x 64 experts,
-// 4 waves as 2 x 2 of 32 x 32; 64-wide K steps staged through LDS, global
-// data loaded two steps ahead.
+// router weight is split exactly into three bf16 parts, w = hi + mid + lo,
+// by truncation: hi keeps the top 8 significant bits of w, mid the top 8 of
+// the exact residual w - hi (at most 16 bits), lo the rest (at most 8 bits,
+// so exact in bf16).  Every product x * part is exact in fp32 and the three
+// MFMAs accumulate them in fp32, as the VALU router's fused multiply-adds do
+// (in another order).  Block: 64 tokens x 64 experts, 4 waves as 2 x 2 of
+// 32 x 32; 64-wide K steps staged through LDS, global data loaded two steps
+// ahead.
 // Named, interleaved fields: adjacent copies from adjacent global addresses
 // are merged into one block copy that the compiler keeps in private memory.
 struct RouterStage {
@@ -773,13 +774,13 @@ struct RouterStage {
 };
 
 MOE_DEV void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  const __bf16 h = (__bf16)w;
-  const float r1 = w - (float)h;
-  const __bf16 m = (__bf16)r1;
-  const __bf16 l = (__bf16)(r1 - (float)m);
-  hi = __builtin_bit_cast(uint16_t, h);
-  mid = __builtin_bit_cast(uint16_t, m);
-  lo = __builtin_bit_cast(uint16_t, l);
+  const uint32_t hb = __float_as_uint(w) & 0xFFFF0000u;
+  const float t1 = w - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(t1) & 0xFFFF0000u;
+  const float t2 = t1 - __uint_as_float(mb);
+  hi = hb >> 16;
+  mid = mb >> 16;
+  lo = __float_as_uint(t2) >> 16;
 }
 
 // Split two fp32 values into packed bf16 pairs of their hi / mid / lo parts.
@@ -828,15 +829,24 @@ MOE_DEV void router_stage(const RouterStage& st, int lrow, int lq, uint4* As, ui
   __syncthreads();
 }
 
+// All 16 fragments of the step are read before the 12 MFMAs: one LDS wait
+// per step instead of one per MFMA (a lone wave per SIMD hides none of it).
 MOE_DEV void router_compute(const uint4* As, const uint4 (*Bs)[64 * 8], int wm, int wn, int lane, f32x16_t& acc) {
+  bf16x8_t a[4], b[4][3];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int chunk = ks * 2 + (lane >> 5);
-    const bf16x8_t a = lds_frag(As, wm * 32 + (lane & 31), chunk);
+    a[ks] = lds_frag(As, wm * 32 + (lane & 31), chunk);
     const int brow = wn * 32 + (lane & 31);
-    acc = mfma(a, lds_frag(Bs[2], brow, chunk), acc);
-    acc = mfma(a, lds_frag(Bs[1], brow, chunk), acc);
-    acc = mfma(a, lds_frag(Bs[0], brow, chunk), acc);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) b[ks][p] = lds_frag(Bs[p], brow, chunk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    acc = mfma(a[ks], b[ks][2], acc);
+    acc = mfma(a[ks], b[ks][1], acc);
+    acc = mfma(a[ks], b[ks][0], acc);
   }
 }
 
@@ -845,7 +855,11 @@ __global__ void __launch_bounds__(256) k_router_mfma(const uint16_t* __restrict_
   __shared__ uint4 As[64 * 8];      // [64 tokens][64 k] bf16, swizzled
   __shared__ uint4 Bs[3][64 * 8];   // hi / mid / lo parts of [64 experts][64 k]
   const int nte = (E + 63) / 64;
-  const int t0 = (blockIdx.x / nte) * 64, e0 = (blockIdx.x % nte) * 64;
+  // consecutive logical tiles on one XCD (block b runs on XCD b % 8): the
+  // expert tiles of one token tile share its activations in that XCD's L2
+  const int nb = gridDim.x;
+  const int lb = nb % 8 == 0 ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int t0 = (lb / nte) * 64, e0 = (lb % nte) * 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   // loaders: token row tid >> 2, 16 bf16 at (tid & 3) * 16; router row tid >> 2, 16 fp32 at (tid & 3) * 16
@@ -854,16 +868,19 @@ __global__ void __launch_bounds__(256) k_router_mfma(const uint16_t* __restrict_
   const float* wrow = wr + (size_t)min(e0 + lrow, E - 1) * H + lq * 16;
   f32x16_t acc = f32x16_t{};
   const int nk = H / 64;
+  // Prefetches are unconditional (step index clamped; the surplus loads at
+  // the end are re-reads): under a branch the compiler waits for every load
+  // in flight, the one just issued included, before each staging.
   RouterStage s0, s1;
   router_load(xrow, wrow, 0, s0);
-  if (nk > 1) router_load(xrow, wrow, 1, s1);
+  router_load(xrow, wrow, min(1, nk - 1), s1);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     router_stage(s0, lrow, lq, As, Bs);
-    if (kt + 2 < nk) router_load(xrow, wrow, kt + 2, s0);
+    router_load(xrow, wrow, min(kt + 2, nk - 1), s0);
     router_compute(As, Bs, wm, wn, lane, acc);
     router_stage(s1, lrow, lq, As, Bs);
-    if (kt + 3 < nk) router_load(xrow, wrow, kt + 3, s1);
+    router_load(xrow, wrow, min(kt + 3, nk - 1), s1);
     router_compute(As, Bs, wm, wn, lane, acc);
   }
   if (kt < nk) {

@@ -129,33 +129,66 @@ __global__ void __launch_bounds__(256) k_perm_hist(const int32_t* __restrict__ i
 }
 
 // One block (1024 threads): per-expert totals and offsets; each histogram
-// entry becomes the exclusive count of earlier chunks for its expert.
+// entry becomes the exclusive count of earlier chunks for its expert.  The
+// chunks are split into G = 1024 / E contiguous groups: thread (g, e) sums
+// group g of expert e with all its loads in flight at once (a batch of 32),
+// the group totals meet in LDS, and each thread then writes its group's
+// running counts from the sum of the groups before it.
+constexpr int kScanBatch = 32;
+
 __global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t* __restrict__ hist,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int gtot[1024];  // [group][expert] totals
   __shared__ int scan_tmp[17];
-  const int e = threadIdx.x;
-  // per expert: exclusive prefix over the chunks (8 loads in flight), written back in place
-  int run = 0;
-  if (e < E) {
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {
-      int v[8];
+  const int tid = threadIdx.x;
+  const int G = max(1, min(1024 / E, nchunks));
+  const int cpg = (nchunks + G - 1) / G;
+  const int e = tid % E, g = tid / E;
+  const bool act = g < G;
+  const int c0 = act ? g * cpg : 0, c1 = act ? min(nchunks, c0 + cpg) : 0;
+  int v[kScanBatch] = {};
+  int sum = 0;
+  for (int c = c0; c < c1; c += kScanBatch) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nchunks ? hist[(size_t)(c0 + u) * E + e] : 0;
+    for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(size_t)(c + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (c0 + u < nchunks) hist[(size_t)(c0 + u) * E + e] = run;
+    for (int u = 0; u < kScanBatch; ++u) sum += v[u];
+  }
+  if (act) gtot[tid] = sum;  // tid == g * E + e
+  __syncthreads();
+  int run = 0, tot = 0;
+  if (act) {
+    for (int q = 0; q < G; ++q) {
+      const int t = gtot[q * E + e];
+      run += q < g ? t : 0;
+      tot += t;
+    }
+    if (c1 - c0 <= kScanBatch) {  // the one batch is still in registers
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (c0 + u < c1) hist[(size_t)(c0 + u) * E + e] = run;
         run += v[u];
+      }
+    } else {
+      for (int c = c0; c < c1; c += kScanBatch) {
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(size_t)(c + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+          if (c + u < c1) hist[(size_t)(c + u) * E + e] = run;
+          run += v[u];
+        }
       }
     }
   }
   // experts' totals -> offsets (block-wide scan); the scatter adds offsets[e]
   int total;
-  const int off = block_exclusive_scan(e < E ? run : 0, scan_tmp, total);
-  if (e < E) {
-    counts[e] = run;
+  const int off = block_exclusive_scan(tid < E ? tot : 0, scan_tmp, total);
+  if (tid < E) {
+    counts[e] = tot;
     offsets[e] = off;
   }
-  if (e == 0) offsets[E] = total;
+  if (tid == 0) offsets[E] = total;
 }
 
 __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,

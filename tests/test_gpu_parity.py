@@ -192,8 +192,11 @@ def test_route_logits_and_ids(T, H, E):
 
 # ------------------------------------------------------------------ permute
 
+# chunk scan shapes: 96 chunks in 4 groups; 5 chunks in 4 groups (last one
+# empty); 64 chunks in one group (two batches); 24 chunks in 10 groups of an E
+# that does not divide 1024 (empty groups at the end)
 @pytest.mark.parametrize("T,k,E", [(1, 6, 256), (4, 6, 32), (64, 6, 256), (4096, 6, 256), (300, 1, 3),
-                                   (77, 8, 1024)])
+                                   (77, 8, 1024), (200, 6, 256), (2048, 8, 1024), (1000, 6, 100)])
 def test_permute_bit_exact(T, k, E):
     print("permute", T, k, E, flush=True)
     rng = np.random.default_rng(T + k + E)

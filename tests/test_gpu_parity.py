@@ -352,6 +352,12 @@ LAYER_CASES = [
     # one token, 7 units of 18 rows per down block: the last block is partial
     ("ragged_H192_I320_T1", 1, 192, 320, 8, 6, 1, 15, True),
     ("ragged_int4_H192_I320_T1", 2, 192, 320, 8, 6, 1, 16, False),
+    # more than 256 experts: the selection by wave maxima (one token: by the
+    # whole block), grouping over up to 1024 experts, the largest k and T
+    ("wide_E1024_k8_T1", 1, 256, 128, 1024, 8, 1, 17, True),
+    ("wide_int4_E1024_k8_T5", 2, 256, 128, 1024, 8, 5, 19, False),
+    ("wide_E300_T64", 1, 256, 128, 300, 6, 64, 20, True),
+    ("wide_E1024_k8_T64", 1, 256, 128, 1024, 8, 64, 21, False),
 ]
 
 

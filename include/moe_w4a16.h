@@ -68,7 +68,8 @@ extern "C" {
 enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, misalignment, bad size, small workspace */
-  MOE_ERR_UNSUPPORTED = -2, /* E > 1024, unknown format or mode */
+  MOE_ERR_UNSUPPORTED = -2, /* E > 1024, a matrix with cols > 3840 or rows > 65536,
+                               unknown format or mode */
   MOE_ERR_HIP = -3          /* a HIP launch failed; see moe_last_error() */
 };
 
@@ -79,7 +80,8 @@ enum { MOE_MODE_AUTO = 0, MOE_MODE_GEMV = 1, MOE_MODE_MFMA = 2 };
 typedef struct moe_w4_matrix {
   int fmt;                   /* MOE_FMT_NVFP4 or MOE_FMT_INT4_G64 */
   int num_experts;           /* E of this stack */
-  int rows, cols;            /* out, in (cols = reduction axis) */
+  int rows, cols;            /* out, in (cols = reduction axis); cols <= 3840 (the GEMV
+                                kernels stage 8 tokens' rows of cols in 64 KB of LDS) */
   const uint8_t* codes;      /* [E, rows, cols/2] */
   const void* scales;        /* NVFP4: uint8 e4m3 [E, rows, cols/16]; INT4: fp16 [E, rows, cols/64] */
   const uint8_t* zeros;      /* INT4: uint8 [E, rows, cols/64]; NVFP4: NULL */

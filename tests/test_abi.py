@@ -102,6 +102,11 @@ def test_grouped_ffn_validation():
     unaligned["down"]["codes"] = FAKE + 8
     expect(inv, moe.moe_grouped_w4a16_ffn, unaligned, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, ws=FAKE,
            ws_bytes=need)
+    # at most 3840 columns per matrix (the header's limit); 3840 itself passes validation
+    need_w = moe.moe_grouped_ffn_workspace_size(4, 3904, 128, 24)
+    msg = expect(uns, moe.moe_grouped_w4a16_ffn, fake_ffn(H=3904), 4, 3904, 128, FAKE, FAKE, 6, FAKE, 24, FAKE,
+                 ws=FAKE, ws_bytes=need_w)
+    assert "3840" in msg
 
 
 def test_layer_decode_validation():

@@ -229,6 +229,7 @@ FFN_CASES = [
     (1, 2048, 768, 256, 6, 5, 51),
     (2, 2048, 768, 256, 6, 3, 52),
     (1, 192, 320, 8, 3, 9, 53),       # K/32 not a multiple of 4: 2 lanes per row
+    (2, 3840, 256, 16, 4, 3, 54),     # the largest K: pieces streamed in chunks
 ]
 
 
@@ -358,6 +359,9 @@ LAYER_CASES = [
     ("wide_int4_E1024_k8_T5", 2, 256, 128, 1024, 8, 5, 19, False),
     ("wide_E300_T64", 1, 256, 128, 300, 6, 64, 20, True),
     ("wide_E1024_k8_T64", 1, 256, 128, 1024, 8, 64, 21, False),
+    # the largest supported hidden size (3840 columns)
+    ("big_H3840_T1", 1, 3840, 512, 64, 4, 1, 22, True),
+    ("big_int4_H3840_T8", 2, 3840, 512, 64, 4, 8, 23, False),
 ]
 
 
@@ -484,6 +488,10 @@ MFMA_CASES = [
     (1, 256, 384, 16, 4, 200, 104, "zipf"),      # LDS-staged 128-row tiles with 64-row remainders
     (1, 2048, 768, 256, 6, 512, 102, "zipf"),
     (2, 2048, 768, 256, 6, 512, 103, "zipf"),
+    # K above 2048 and I not a multiple of 128: the LDS-staged 128-row tile kernels, both formats
+    (2, 3840, 256, 16, 4, 300, 105, "zipf"),
+    (1, 3840, 512, 8, 2, 200, 106, "uniform"),
+    (2, 256, 192, 8, 3, 300, 107, "zipf"),
 ]
 
 

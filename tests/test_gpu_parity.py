@@ -492,6 +492,8 @@ MFMA_CASES = [
     (2, 3840, 256, 16, 4, 300, 105, "zipf"),
     (1, 3840, 512, 8, 2, 200, 106, "uniform"),
     (2, 256, 192, 8, 3, 300, 107, "zipf"),
+    # 1024 experts, k = 8: the tile table's widest scan, most experts with one or no tile
+    (1, 256, 128, 1024, 8, 300, 108, "uniform"),
 ]
 
 

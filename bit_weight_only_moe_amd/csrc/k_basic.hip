@@ -191,22 +191,35 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t*
   if (tid == 0) offsets[E] = total;
 }
 
+// Rank of each pair among the earlier pairs of its chunk with the same
+// expert: inside the wave from a match mask (one ballot per bit of the
+// expert id and a valid bit, E <= 1024), plus the counts of that expert in
+// the chunk's earlier waves (each wave's lowest lane of a value stores it).
 __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ base,
                                                       int32_t* __restrict__ sorted_pairs,
                                                       int32_t* __restrict__ pair_pos) {
-  __shared__ int32_t cid[kPermChunk];
-  const int p0 = blockIdx.x * kPermChunk;
-  const int i = threadIdx.x;
-  const int p = p0 + i;
-  cid[i] = (p < n) ? ids[p] : -1;
+  __shared__ int32_t wcnt[4 * 1024];  // [wave][expert]
+  const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
+  const int p = blockIdx.x * kPermChunk + i;
+  for (int j = i; j < 4 * E; j += 256) wcnt[j] = 0;
+  const int v = p < n ? ids[p] : 1024;  // 1024: no pair (never an expert id)
+  unsigned long long m = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 11; ++b) {
+    const bool bit = (v >> b) & 1;
+    const unsigned long long bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  const int rw = __popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (p < n && rw == 0) wcnt[wave * E + v] = __popcll(m);
   __syncthreads();
   if (p >= n) return;
-  const int e = cid[i];
-  int rank = 0;
-  for (int q = 0; q < i; ++q) rank += (cid[q] == e);
-  const int pos = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
+  int rank = rw;
+  for (int w = 0; w < wave; ++w) rank += wcnt[w * E + v];
+  const int pos = offsets[v] + base[(size_t)blockIdx.x * E + v] + rank;
   sorted_pairs[pos] = p;
   pair_pos[p] = pos;
 }

@@ -128,24 +128,23 @@ __global__ void __launch_bounds__(256) k_perm_hist(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block (1024 threads): per-expert totals and offsets; each histogram
-// entry becomes the exclusive count of earlier chunks for its expert.  The
-// chunks are split into G = 1024 / E contiguous groups: thread (g, e) sums
-// group g of expert e with all its loads in flight at once (a batch of 32),
-// the group totals meet in LDS, and each thread then writes its group's
-// running counts from the sum of the groups before it.
+// Per-expert running counts over the chunks: each histogram entry becomes
+// the count of its expert in the earlier chunks, and counts[e] the total.
+// Block b takes experts [64b, 64b + 64): wave g sums the g-th quarter of the
+// chunks for its 64 experts with all its loads in flight at once (a batch of
+// 32), the quarter totals meet in LDS, and each wave then writes its
+// quarter's running counts.  Small blocks (256 threads) fit beside the
+// matrix-core kernels that may share the chip.
 constexpr int kScanBatch = 32;
 
-__global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t* __restrict__ hist,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int gtot[1024];  // [group][expert] totals
-  __shared__ int scan_tmp[17];
-  const int tid = threadIdx.x;
-  const int G = max(1, min(1024 / E, nchunks));
-  const int cpg = (nchunks + G - 1) / G;
-  const int e = tid % E, g = tid / E;
-  const bool act = g < G;
-  const int c0 = act ? g * cpg : 0, c1 = act ? min(nchunks, c0 + cpg) : 0;
+__global__ void __launch_bounds__(256) k_perm_scan(int nchunks, int E, int32_t* __restrict__ hist,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int gtot[256];  // [quarter][expert of the block]
+  const int tid = threadIdx.x, el = tid & 63, g = tid >> 6;
+  const int e = blockIdx.x * 64 + el;
+  const bool act = e < E;
+  const int cpg = (nchunks + 3) / 4;
+  const int c0 = g * cpg, c1 = act ? min(nchunks, c0 + cpg) : 0;
   int v[kScanBatch] = {};
   int sum = 0;
   for (int c = c0; c < c1; c += kScanBatch) {
@@ -154,57 +153,75 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int nchunks, int E, int32_t*
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) sum += v[u];
   }
-  if (act) gtot[tid] = sum;  // tid == g * E + e
+  gtot[tid] = sum;
   __syncthreads();
+  if (!act) return;
   int run = 0, tot = 0;
-  if (act) {
-    for (int q = 0; q < G; ++q) {
-      const int t = gtot[q * E + e];
-      run += q < g ? t : 0;
-      tot += t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = gtot[q * 64 + el];
+    run += q < g ? t : 0;
+    tot += t;
+  }
+  if (g == 0) counts[e] = tot;
+  if (c1 - c0 <= kScanBatch) {  // the one batch is still in registers
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      if (c0 + u < c1) hist[(size_t)(c0 + u) * E + e] = run;
+      run += v[u];
     }
-    if (c1 - c0 <= kScanBatch) {  // the one batch is still in registers
+  } else {
+    for (int c = c0; c < c1; c += kScanBatch) {
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(size_t)(c + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < kScanBatch; ++u) {
-        if (c0 + u < c1) hist[(size_t)(c0 + u) * E + e] = run;
+        if (c + u < c1) hist[(size_t)(c + u) * E + e] = run;
         run += v[u];
-      }
-    } else {
-      for (int c = c0; c < c1; c += kScanBatch) {
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(size_t)(c + u) * E + e] : 0;
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) {
-          if (c + u < c1) hist[(size_t)(c + u) * E + e] = run;
-          run += v[u];
-        }
       }
     }
   }
-  // experts' totals -> offsets (block-wide scan); the scatter adds offsets[e]
-  int total;
-  const int off = block_exclusive_scan(tid < E ? tot : 0, scan_tmp, total);
-  if (tid < E) {
-    counts[e] = tot;
-    offsets[e] = off;
-  }
-  if (tid == 0) offsets[E] = total;
 }
 
-// Rank of each pair among the earlier pairs of its chunk with the same
-// expert: inside the wave from a match mask (one ballot per bit of the
-// expert id and a valid bit, E <= 1024), plus the counts of that expert in
-// the chunk's earlier waves (each wave's lowest lane of a value stores it).
+// Every block first turns the experts' counts into their offsets (one block
+// scan over E <= 1024 counts; block 0 publishes them).  Then the rank of each
+// pair among its chunk's earlier pairs of the same expert: inside the wave
+// from a match mask (one ballot per bit of the expert id and a valid bit),
+// plus the counts of that expert in the chunk's earlier waves (each wave's
+// lowest lane of a value stores it).
 __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,
-                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ sorted_pairs,
                                                       int32_t* __restrict__ pair_pos) {
   __shared__ int32_t wcnt[4 * 1024];  // [wave][expert]
+  __shared__ int32_t s_off[1024];
+  __shared__ int scan_tmp[17];
   const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   const int p = blockIdx.x * kPermChunk + i;
-  for (int j = i; j < 4 * E; j += 256) wcnt[j] = 0;
   const int v = p < n ? ids[p] : 1024;  // 1024: no pair (never an expert id)
+  int c4[4], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = i * 4 + q;
+    c4[q] = counts[min(e, E - 1)];
+    c4[q] = e < E ? c4[q] : 0;
+    loc += c4[q];
+  }
+  for (int j = i; j < 4 * E; j += 256) wcnt[j] = 0;
+  int total;
+  int pre = block_exclusive_scan(loc, scan_tmp, total);  // its barriers also order the zeroing
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = i * 4 + q;
+    if (e < E) {
+      s_off[e] = pre;
+      if (blockIdx.x == 0) offsets[e] = pre;
+    }
+    pre += c4[q];
+  }
+  if (blockIdx.x == 0 && i == 0) offsets[E] = total;
   unsigned long long m = ~0ull;
 #pragma unroll
   for (int b = 0; b < 11; ++b) {
@@ -213,13 +230,12 @@ __global__ void __launch_bounds__(256) k_perm_scatter(const int32_t* __restrict_
     m &= bit ? bb : ~bb;
   }
   const int rw = __popcll(m & ((1ull << lane) - 1ull));
-  __syncthreads();
   if (p < n && rw == 0) wcnt[wave * E + v] = __popcll(m);
   __syncthreads();
   if (p >= n) return;
   int rank = rw;
   for (int w = 0; w < wave; ++w) rank += wcnt[w * E + v];
-  const int pos = offsets[v] + base[(size_t)blockIdx.x * E + v] + rank;
+  const int pos = s_off[v] + base[(size_t)blockIdx.x * E + v] + rank;
   sorted_pairs[pos] = p;
   pair_pos[p] = pos;
 }
@@ -248,9 +264,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   int32_t* hist = (int32_t*)ws;
   hipLaunchKernelGGL(k_perm_hist, dim3(nchunks), dim3(kPermChunk), E * sizeof(int32_t), s, ids, n, E, hist);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, nchunks, E, hist, counts, offsets);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, offsets, hist, sorted_pairs,
-                     pair_pos);
+  hipLaunchKernelGGL(k_perm_scan, dim3((E + 63) / 64), dim3(256), 0, s, nchunks, E, hist, counts);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, counts, hist, offsets,
+                     sorted_pairs, pair_pos);
   if (x && x_perm) hipLaunchKernelGGL(k_gather_rows, dim3(n), dim3(256), 0, s, x, sorted_pairs, k, H, x_perm);
   return hipGetLastError();
 }

@@ -291,10 +291,10 @@ def bench_prefill(args, fmt):
     f_shared = [moe.ffn_weights(l["shared"]) for l in layers]
 
     # The shared expert needs no routing: its grouped FFN runs on a side stream
-    # (own workspace), forked after the router GEMM, alongside the top-k and
-    # permute kernels, which leave most of the chip idle, and the start of the
-    # routed FFN; both join before the combine.  (Forked before the router it
-    # slows the router about as much as it gains: 8 us more per step.)
+    # (own workspace), forked after the top-k, alongside the permute kernels,
+    # which leave most of the chip idle, and the start of the routed FFN; both
+    # join before the combine.  (Forked before the router it slows the router
+    # about as much as it gains; forked before the top-k it slows the top-k.)
     side = torch.cuda.Stream()
     gws_s = torch.empty(gws_n, dtype=torch.uint8, device=dev)
 
@@ -310,8 +310,8 @@ def bench_prefill(args, fmt):
     def step(i, s):
         L = layers[i % R]
         moe.moe_route(x, L["w_router"], T, H, E, k, lg, ids, w, stream=s)   # router GEMM (timed; skewed logits route)
-        shared_ffn(i, s)
         moe.moe_topk_softmax(zl, T, E, k, ids, w, stream=s)
+        shared_ffn(i, s)
         moe.moe_permute(ids, T, k, E, counts, offsets, sp, pp, None, None, 0, pws, pws_n, stream=s)
         routed_ffn(i, s)
         s.wait_stream(side)

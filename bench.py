@@ -36,7 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # (profiles/hbm_traffic_counters.md).  Workloads not listed report null.
 TRAFFIC_BYTES = {
     ("decode_b1", "nvfp4"): 21.75e6,
-    ("decode_T16", "nvfp4"): 223.4e6,
+    ("decode_T16", "nvfp4"): 222.9e6,
     ("prefill", "nvfp4"): 1239.0e6,
 }
 

@@ -28,6 +28,7 @@ EXPORTED = [
     "moe_abi_version", "moe_last_error", "moe_dequant_w4", "moe_route", "moe_topk_softmax",
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_ffn_workspace_size",
     "moe_grouped_w4a16_ffn", "moe_combine", "moe_layer_decode_workspace_size", "moe_layer_decode",
+    "moe_rms_norm",
 ]
 
 
@@ -72,6 +73,7 @@ def _load():
         "moe_combine": (I, [P, P, P, P, P, I, I, I, P, P, S]),
         "moe_layer_decode_workspace_size": (Z, [ctypes.POINTER(LayerWeights), I]),
         "moe_layer_decode": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, P, Z, S]),
+        "moe_rms_norm": (I, [P, I, I, ctypes.c_float, P, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,3 +186,7 @@ def moe_layer_decode(layer, x, residual, T, y, ids_out=None, w_out=None, ws=None
     L = layer if isinstance(layer, Layer) else Layer(layer)
     return _check(_lib.moe_layer_decode(ctypes.byref(L.c), _ptr(x), _ptr(residual), T, _ptr(y), _ptr(ids_out),
                                         _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_rms_norm(r, T, H, eps, x, stream=None):
+    return _check(_lib.moe_rms_norm(_ptr(r), T, H, float(eps), _ptr(x), _stream(stream)))

@@ -181,11 +181,15 @@ int moe_route(const uint16_t* x, const float* w_router, int T, int H, int E, int
   if (rc) return rc;
   if (H < 64 || H % 64) return fail(MOE_ERR_INVALID_ARG, "moe_route: H=%d is not a positive multiple of 64", H);
   if (!x || !w_router || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "moe_route: null argument");
-  if (!logits_out) return fail(MOE_ERR_INVALID_ARG, "moe_route: logits_out is required as scratch (fp32 [T, E])");
   if (!aligned16(x) || !aligned16(w_router))
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x / w_router not 16-byte aligned");
+  if (!logits_out && moe::route_lds_tokens(H, E) == 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d, E=%d too large to keep the logits on chip (pass logits_out)",
+                H, E);
   if (T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
+  if (!logits_out)
+    return hip_status(moe::launch_route_topk_lds(x, w_router, T, H, E, k, topk_ids, topk_w, s), "moe_route");
   hipError_t e = moe::launch_router_logits(x, w_router, T, H, E, logits_out, s);
   if (e == hipSuccess) e = moe::launch_topk_softmax(logits_out, T, E, k, topk_ids, topk_w, s);
   return hip_status(e, "moe_route");
@@ -295,6 +299,16 @@ int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* top
   return hip_status(moe::launch_combine(out_perm, pair_pos, topk_w, out_shared, residual, T, k, H, y, y_f32,
                                         as_stream(stream)),
                     "moe_combine");
+}
+
+int moe_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, void* stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_rms_norm: T=%d < 0", T);
+  if (H < 64 || H % 64) return fail(MOE_ERR_INVALID_ARG, "moe_rms_norm: H=%d is not a positive multiple of 64", H);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MOE_ERR_INVALID_ARG, "moe_rms_norm: eps must be finite and >= 0");
+  if (!r || !x) return fail(MOE_ERR_INVALID_ARG, "moe_rms_norm: null argument");
+  if (!aligned16(r) || !aligned16(x)) return fail(MOE_ERR_INVALID_ARG, "moe_rms_norm: r / x not 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_rms_norm(r, T, H, eps, x, as_stream(stream)), "moe_rms_norm");
 }
 
 static int check_layer(const moe_layer_weights* L, const char* who) {

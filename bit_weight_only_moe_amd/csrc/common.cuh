@@ -142,9 +142,13 @@ namespace moe {
 // ---- device-coherent accesses for data exchanged between blocks ---------
 // Agent-scope relaxed atomic loads/stores are coherent across the chip's
 // separate L2 caches without the cache write-back / invalidate that an
-// agent-scope fence implies.  A producer stores with st_dev, waits for its
-// stores to complete (workgroup-scope release), then bumps a counter; a
-// consumer polls the counter and then reads with ld_dev.
+// agent-scope fence implies: on gfx950 they carry the device-scope cache
+// policy bit (sc1), so a store is written through to the device-coherent
+// level and is acknowledged (its vmcnt decrement) only once it is there.
+// A producer block stores with st_dev, then block_stores_done() (every wave
+// waits for its own stores, then the block barrier), then one thread bumps
+// a counter; the consumer that sees the final count issues an agent-scope
+// acquire before it reads.
 MOE_DEV void st_dev(int32_t* p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MOE_DEV void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -164,6 +168,17 @@ MOE_DEV float ld_dev(const float* p) {
 }
 MOE_DEV uint64_t ld_dev(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wave of the block waits until all of its own outstanding vector
+// memory operations, st_dev stores included, have completed; the barrier
+// then orders all of those waits before whatever one thread does next (the
+// ticket atomic).  A workgroup-scope release fence would not do here: on
+// this target, outside thread-group-split mode, it waits for LDS traffic
+// only and leaves global stores in flight.
+MOE_DEV void block_stores_done() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 }  // namespace moe

@@ -62,6 +62,7 @@ hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* cod
 // Block: 4 waves = 4 experts; up to kRouteTok tokens staged in LDS as bf16
 // (at most 64 KB).
 constexpr int kRouteTok = 16;
+constexpr int kRouteT4 = 4;  // tokens per block when the logits stay in LDS
 constexpr int kRouterMfmaMinT = 256;
 
 __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restrict__ x, const float* __restrict__ wr,
@@ -109,6 +110,59 @@ __global__ void __launch_bounds__(256) k_topk_softmax(const float* __restrict__ 
 
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   hipLaunchKernelGGL(k_topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- router + top-k, logits on chip
+// moe_route without a logits buffer: one block per batch of tpb <= 4 tokens
+// computes the batch's logits against every expert (wave w takes experts w,
+// w + 4, ...; the same per-expert dot product as k_router_logits, so the
+// logits are the same bits), keeps them in LDS and selects each token's top
+// k with one wave per token.  Every block re-reads the router weights (from
+// L2), which is the price of not writing the logits out.
+__global__ void __launch_bounds__(256) k_route_topk_lds(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                        int T, int H, int E, int k, int tpb,
+                                                        int32_t* __restrict__ ids, float* __restrict__ w) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0);
+  uint16_t* xs = (uint16_t*)smem;                             // [tpb][H]
+  float* s_log = (float*)(smem + (size_t)tpb * H * 2);        // [tpb][E]
+  uint64_t* rk = (uint64_t*)(smem + (((size_t)tpb * H * 2 + (size_t)tpb * E * 4 + 15) & ~(size_t)15));
+  copy_to_lds((uint4*)xs, (const uint4*)(x + (size_t)t0 * H), nt * H / 8);
+  __syncthreads();
+  for (int e = wave; e < E; e += 4) {
+    float4 wv[kRouterC];
+    router_prefetch(wr + (size_t)e * H, H, lane, wv);
+    float acc[kRouteT4];
+    router_dots<kRouteT4>(wr + (size_t)e * H, xs, H, nt, lane, acc, wv);
+#pragma unroll
+    for (int t = 0; t < kRouteT4; ++t)
+      if (t < nt && lane == 63) s_log[t * E + e] = acc[t];
+  }
+  __syncthreads();
+  if (wave >= nt) return;
+  const int t = t0 + wave;
+  if (E <= 256)
+    wave_topk_rank(s_log + wave * E, E, k, lane, rk + wave * kWaveRankScratch, ids + (size_t)t * k, w + (size_t)t * k);
+  else
+    wave_topk_softmax(s_log + wave * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+// Tokens per block of k_route_topk_lds within 64 KB of LDS (0: H too large).
+int route_lds_tokens(int H, int E) {
+  for (int tpb = kRouteT4; tpb >= 1; --tpb) {
+    const size_t lds = (((size_t)tpb * H * 2 + (size_t)tpb * E * 4 + 15) & ~(size_t)15) + 4 * kWaveRankScratch * 8;
+    if (lds <= 64 * 1024) return tpb;
+  }
+  return 0;
+}
+
+hipError_t launch_route_topk_lds(const uint16_t* x, const float* wr, int T, int H, int E, int k, int32_t* ids,
+                                 float* w, hipStream_t s) {
+  const int tpb = route_lds_tokens(H, E);
+  const size_t lds = (((size_t)tpb * H * 2 + (size_t)tpb * E * 4 + 15) & ~(size_t)15) + 4 * kWaveRankScratch * 8;
+  hipLaunchKernelGGL(k_route_topk_lds, dim3((T + tpb - 1) / tpb), dim3(256), lds, s, x, wr, T, H, E, k, tpb, ids, w);
   return hipGetLastError();
 }
 
@@ -316,6 +370,50 @@ hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const 
                           const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
   hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, out_perm, pair_pos, w, out_shared, residual, k, H, y, y_f32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- chain normalisation
+// x[t] = bf16(r[t] / sqrt(mean_h(r[t]^2) + eps)), one block per token.  Each
+// bf16 square is exact in fp32; a thread sums its squares in ascending
+// column order, the waves' sums are added in wave order, and each element
+// is divided by the rounded root and rounded to bf16 (nearest, ties to
+// even).  Every thread writes only the elements it read, after the block's
+// sum is complete, so x may alias r.
+__global__ void __launch_bounds__(256) k_rms_norm(const uint16_t* r, int H, float eps, uint16_t* x) {
+  __shared__ float part[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint4* rr = (const uint4*)(r + (size_t)blockIdx.x * H);
+  uint4* xx = (uint4*)(x + (size_t)blockIdx.x * H);
+  const int n8 = H / 8;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = rr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_to_f32(w[q] & 0xffffu), b = bf16_to_f32(w[q] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) part[wave] = ss;
+  __syncthreads();
+  const float s = sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H + eps);
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = rr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = f32_to_bf16_rne(bf16_to_f32(w[q] & 0xffffu) / s) | (f32_to_bf16_rne(bf16_to_f32(w[q] >> 16) / s) << 16);
+    xx[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, hipStream_t s) {
+  hipLaunchKernelGGL(k_rms_norm, dim3(T), dim3(256), 0, s, r, H, eps, x);
   return hipGetLastError();
 }
 

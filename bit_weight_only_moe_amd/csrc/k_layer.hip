@@ -35,20 +35,6 @@
 
 namespace moe {
 
-#ifdef MOE_TRACE
-// Per-block phase timestamps (100 MHz constant clock) for development builds.
-__device__ unsigned long long g_trace[3][65536 * 8];
-#define MOE_TRACE_AT(kern, slot)                                                      \
-  do {                                                                                \
-    if (threadIdx.x == 0 && blockIdx.x < 65536)                                       \
-      g_trace[kern][blockIdx.x * 8 + (slot)] = __builtin_amdgcn_s_memrealtime();      \
-  } while (0)
-#else
-#define MOE_TRACE_AT(kern, slot) \
-  do {                           \
-  } while (0)
-#endif
-
 // Rows per block (measured: 8 or 32 gate/up rows, 32 or 128 down rows are
 // slower from 4 to 64 tokens).
 constexpr int kRG = 16;      // gate/up rows per block (4 when T == 1)
@@ -151,7 +137,6 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
     __syncthreads();
     stage_rows<FMT>(xs, xsum, x, [&](int t) { return tok_of(rb + t); }, nt, H);
     __syncthreads();
-    MOE_TRACE_AT(kern, 2);
     float ag[NT], au[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
@@ -189,7 +174,6 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
       }
     }
   }
-  MOE_TRACE_AT(kern, 3);
 }
 
 // ------------------------------------------------------------------ down
@@ -225,7 +209,6 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
     __syncthreads();
     stage_rows<FMT>(xs, xsum, hin, [rb](int t) { return rb + t; }, nt, K);
     __syncthreads();
-    MOE_TRACE_AT(2, 2);
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
@@ -278,7 +261,6 @@ template <int FMT, int NT>
 __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int ticket;
-  MOE_TRACE_AT(0, 0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, E = a.E;
   if ((int)blockIdx.x >= a.nR) {
@@ -287,7 +269,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     const int i0 = slice * a.rg, i1 = min(a.Is, i0 + a.rg);
     gateup_rows<FMT, NT>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x, [](int r) { return r; },
                          a.h_shared, a.Is, a.lpr_h, smem, 0);
-    MOE_TRACE_AT(0, 4);
     return;
   }
   const int nb = a.nR / a.nRe;  // token batches
@@ -301,7 +282,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     router_prefetch(a.w_router + (size_t)min(e, E - 1) * H, H, lane, wv);
     copy_to_lds((uint4*)smem, (const uint4*)(a.x + (size_t)t0 * H), nt * H / 8);
     __syncthreads();
-    MOE_TRACE_AT(0, 1);
     if (e < E) {
       constexpr int RT = NT == 1 ? 1 : kRouteT;  // a lone token computes one chain
       float acc[RT];
@@ -312,13 +292,10 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
         if (t < nt && lane == 63) st_dev(a.logits + (size_t)(t0 + t) * E + e, acc[t]);
     }
   }
-  MOE_TRACE_AT(0, 2);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this block's stores are complete
-  __syncthreads();
+  block_stores_done();  // every logit this block stored is visible chip-wide
   int* ctr = a.sync + kTicketBatch + 16 * batch;
   if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  MOE_TRACE_AT(0, 3);
   if (ticket != a.nRe - 1) return;
 
   // Last router block of this token batch: every logit of its nt <= 4 tokens
@@ -328,7 +305,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     *ctr = 0;  // ready for the next call
   }
   __syncthreads();
-  MOE_TRACE_AT(0, 5);
   const int k = a.k, n = T * k;
   // Byte offsets into smem: pointers formed as smem + offset stay LDS
   // pointers for the compiler (an integer round trip would turn every access
@@ -348,7 +324,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   uint64_t* rk = (uint64_t*)(smem + o_rk);                        // [kRankScratch]
   copy_f32_to_lds(s_log, a.logits + (size_t)t0 * E, nt * E);
   __syncthreads();
-  if (nb == 1) MOE_TRACE_AT(0, 7);
   // a lone token: all four waves share its selection (rank counting for up
   // to 256 experts); several tokens: one per wave (rank counting over the
   // lanes' largest keys for up to 256 experts, else k rounds of a wave maximum)
@@ -362,7 +337,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   else if (wave < nt)
     wave_topk_softmax(s_log + wave * E, E, k, lane, s_ids + (t0 + wave) * k, s_w + (t0 + wave) * k);
   __syncthreads();
-  MOE_TRACE_AT(0, 6);
   const int p0 = t0 * k, p1 = (t0 + nt) * k;  // this batch's pairs
   if (nb > 1) {
     // Publish this batch's choices; the last batch to finish groups all tokens.
@@ -370,8 +344,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
       st_dev(a.ids + p, s_ids[p]);
       st_dev(a.w + p, s_w[p]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
+    block_stores_done();
     if (tid == 0)
       ticket = __hip_atomic_fetch_add(a.sync + kTicketGroup, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -388,7 +361,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
       }
     }
     __syncthreads();
-    MOE_TRACE_AT(0, 7);
   }
 
   if (T == 1) {
@@ -413,7 +385,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
       }
     }
     if (tid == 0) a.n_active[0] = k;
-    MOE_TRACE_AT(0, 4);
     return;
   }
 
@@ -478,7 +449,6 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
       a.w_out[p] = s_w[p];
     }
   }
-  MOE_TRACE_AT(0, 4);
 }
 
 // ------------------------------------------------------------------ launch 2
@@ -490,18 +460,15 @@ template <int FMT, int NT>
 __global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_layer_gateup(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
-  MOE_TRACE_AT(1, 0);
   const int unit = blockIdx.x / a.slices_r;
   if (threadIdx.x < kRec) s_rec[threadIdx.x] = a.rec[(size_t)unit * kRec + threadIdx.x];
   __syncthreads();
-  MOE_TRACE_AT(1, 1);
   const int e = s_rec[0];
   if (e < 0) return;
   const int r0 = s_rec[1];
   const int i0 = (blockIdx.x % a.slices_r) * a.rg, i1 = min(a.I, i0 + a.rg);
   gateup_rows<FMT, NT>(a.gate, a.up, e, r0, r0 + s_rec[2], i0, i1, a.H, a.x,
                        [r0](int r) { return s_rec[4 + r - r0]; }, a.h_routed, a.I, a.lpr_h, smem, 1);
-  MOE_TRACE_AT(1, 4);
 }
 
 // ------------------------------------------------------------------ launch 3
@@ -514,7 +481,6 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
   __shared__ int ticket, s_nact;
-  MOE_TRACE_AT(2, 0);
   const int tid = threadIdx.x;
   const int T = a.T, H = a.H, k = a.k, n = T * k;
   // the shared expert's units come first: they carry NT tokens each and
@@ -533,7 +499,6 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     s_pp[p] = a.pair_pos[p];
   }
   __syncthreads();
-  MOE_TRACE_AT(2, 1);
   const int n0 = slice * a.rd, n1 = min(H, n0 + a.rd);
   if (routed) {
     const int e = s_rec[0];
@@ -544,14 +509,11 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     const int r0 = unit * NT;
     down_rows<FMT, NT>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared, a.lpr_is, true, smem);
   }
-  MOE_TRACE_AT(2, 3);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
+  block_stores_done();
   const int units = s_nact + a.nsb;
   int* ctr = a.sync + kTicketSlice + 16 * slice;
   if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  MOE_TRACE_AT(2, 4);
   if (ticket != units - 1) return;
   // last block of this slice: every unit's rows [n0, n1) are stored
   if (tid == 0) {
@@ -612,7 +574,6 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     rounds(std::integral_constant<int, 2>{});
   else
     rounds(std::integral_constant<int, 4>{});
-  MOE_TRACE_AT(2, 5);
 }
 
 // ------------------------------------------------------------------ launch 3, one token
@@ -632,7 +593,6 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   __shared__ float s_w[kMaxUnitsT1];
   __shared__ int s_pp[kMaxUnitsT1];
   __shared__ float s_o[kT1Threads];  // [unit][row]: units * R <= lane groups <= threads
-  MOE_TRACE_AT(2, 0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = a.H, I = a.I, k = a.k, R = a.rows_t1;
   const bool has_shared = a.nsb > 0;
@@ -648,7 +608,6 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
     s_pp[tid] = 0;
   }
   __syncthreads();
-  MOE_TRACE_AT(2, 1);
   const int lpr = a.lpr_i, rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
   const int ppl = (I / 32) / lpr;
   const int d = wave * rpw + rsub;  // this lane group's row-dot: unit d / R, row n0 + d % R
@@ -691,7 +650,6 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   if (hp1 < total) h_store(hp1, hv1);
   for (int p = tid + 2 * kT1Threads; p < total; p += kT1Threads) h_store(p, h_piece(p));
   __syncthreads();
-  MOE_TRACE_AT(2, 2);
   float acc[1] = {0.f};
 #pragma unroll
   for (int q = 0; q < kMaxPcD; ++q)
@@ -699,7 +657,6 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   acc[0] = group_sum_last_dyn(acc[0], lpr);
   if (active && lir == lpr - 1) s_o[d] = acc[0] * tensor_scale<FMT>(D, e);
   __syncthreads();
-  MOE_TRACE_AT(2, 3);
   if (tid < R && n0 + tid < H) {
     const int c = n0 + tid;
     // every LDS read issued before the first use (a chain of dependent
@@ -719,7 +676,6 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
     if (a.residual) acc2 += bf16_to_f32(a.residual[c]);
     a.y[c] = (uint16_t)f32_to_bf16_rne(acc2);
   }
-  MOE_TRACE_AT(2, 4);
 }
 
 // ------------------------------------------------------------------ grouped FFN (composed path)
@@ -949,11 +905,3 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
 }
 
 }  // namespace moe
-
-#ifdef MOE_TRACE
-extern "C" void* moe_trace_ptr() {
-  void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(moe::g_trace)) != hipSuccess) return nullptr;
-  return p;
-}
-#endif

@@ -423,25 +423,6 @@ __global__ void __launch_bounds__(256, (WM == 1 && FMT == kFmtNvfp4) ? 3 : 2) k_
 // !GU: columns n0 + wave*64 + cf*32 + l%32 (the block covers 256 outputs).
 constexpr int kBdMaxSteps = 32;  // K <= 2048
 
-#ifdef MOE_TRACE
-// Per-block phase timestamps (100 MHz constant clock) for development builds.
-__device__ unsigned long long g_trace_bd[2][65536 * 8];
-#define MOE_TRACE_BD(kern, slot)                                                      \
-  do {                                                                                \
-    if (threadIdx.x == 0 && blockIdx.x < 65536)                                       \
-      g_trace_bd[kern][blockIdx.x * 8 + (slot)] = __builtin_amdgcn_s_memrealtime();   \
-  } while (0)
-extern "C" void* moe_trace_bd_ptr() {
-  void* p = nullptr;
-  (void)hipGetSymbolAddress(&p, HIP_SYMBOL(g_trace_bd));
-  return p;
-}
-#else
-#define MOE_TRACE_BD(kern, slot) \
-  do {                           \
-  } while (0)
-#endif
-
 // NVFP4 needs K to be a whole number of 4-step groups.
 static inline bool bd_k_ok(int fmt, int K) {
   return K <= kBK * kBdMaxSteps && (fmt != kFmtNvfp4 || K % (4 * kBK) == 0);
@@ -458,7 +439,6 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   block_tile_chunked(N / NB, g.tiles[0], tile, slice);
   int e, r0, r1;
   if (!tile_of(g, tile, e, r0, r1)) return;
-  MOE_TRACE_BD(GU ? 0 : 1, 0);
   const int n0 = slice * NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Activations: load v of a thread is row v * 32 + tid / 8, 16-byte chunk
@@ -532,7 +512,6 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
   load_b(min(3, nk - 1), 3);
   write_a(0, 0);
   __syncthreads();
-  MOE_TRACE_BD(GU ? 0 : 1, 1);
   auto step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int kt = decltype(kc)::value, j = kt % D;
     write_a((j + 1) % D, (kt + 1) & 1);  // after the last step: unused
@@ -569,15 +548,10 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
         acc[1][rf][i] = fmaf(s1, part[1][rf][i], acc[1][rf][i]);
       }
     __syncthreads();
-    if (kt == 0) MOE_TRACE_BD(GU ? 0 : 1, 2);
-    if (kt == 3) MOE_TRACE_BD(GU ? 0 : 1, 3);
-    if (kt == 7) MOE_TRACE_BD(GU ? 0 : 1, 4);
-    if (kt == 11) MOE_TRACE_BD(GU ? 0 : 1, 5);
   };
   // Straight-line code (no loop back edge): the compiler then waits for each
   // step's own loads only, not for every load in flight.
   unrolled_steps<0, kBdMaxSteps>(nk, step);
-  MOE_TRACE_BD(GU ? 0 : 1, 6);
   if (GU) {
     const int f = n0 + wave * 32 + l32;
 #pragma unroll

@@ -18,6 +18,11 @@ hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* cod
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, int E, float* logits, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                                 hipStream_t s);
+// Router and top-k in one kernel, the logits kept in LDS (moe_route without
+// a logits buffer); route_lds_tokens() == 0 means H is too large for it.
+int route_lds_tokens(int H, int E);
+hipError_t launch_route_topk_lds(const uint16_t* x, const float* wr, int T, int H, int E, int k, int32_t* ids,
+                                 float* w, hipStream_t s);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
@@ -25,6 +30,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
                           void* ws, hipStream_t s);
 hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const float* w, const float* out_shared,
                           const uint16_t* residual, int T, int k, int H, uint16_t* y, float* y_f32, hipStream_t s);
+hipError_t launch_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, hipStream_t s);
 hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, hipStream_t s);
 hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, const int32_t* offsets,
                                const int32_t* sorted_pairs, int k, int max_active, const uint16_t* x, int H, int I,

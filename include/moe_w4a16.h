@@ -105,24 +105,44 @@ typedef struct moe_layer_weights {
 int moe_abi_version(void);
 const char* moe_last_error(void);
 
-/* Dequantise expert `expert` of matrix `m` to fp32 out[rows, cols].
- * Exact: NVFP4 gives the single fp32 rounding of tensor_scale*e4m3*e2m1,
- * INT4 gives scale*(code-zero) exactly.  (Test export of the format
- * definition above.) */
+/* Dequantise expert `expert` of matrix `m` to fp32 out[rows, cols] (device,
+ * caller-owned, 16-byte aligned).  Exact: NVFP4 gives the single fp32
+ * rounding of tensor_scale*e4m3*e2m1, INT4 gives scale*(code-zero) exactly.
+ * The formats are the NVFP4 checkpoint served weight-only as W4A16 of
+ * "[Model] Add Flint (RecursiveSI/flint)", section "What happened", and the
+ * group-64 affine INT4 of "Recursive Flint: 125 tok/s on an M4 Pro,
+ * measured where it matters least", table under "What actually shipped".
+ * Errors: MOE_ERR_INVALID_ARG for a null or misaligned pointer or an expert
+ * outside [0, num_experts); MOE_ERR_UNSUPPORTED for an unknown format.
+ * (A test export: it states the format definition above as code.) */
 int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream);
 
 /* Router: logits[t, e] = sum_h x[t, h] * w_router[e, h] (fp32 accumulation)
- * for x bf16 [T, H], then top-k and softmax weights as in moe_topk_softmax.
- * logits_out fp32 [T, E] is required and receives the logits.  topk_ids
- * int32 [T, k] in rank order,
- * topk_w fp32 [T, k].  Source: the fused top-k router of "[Model] Add Flint
- * (RecursiveSI/flint)", section "What happened". */
+ * for x bf16 [T, H] and w_router fp32 [E, H] (both 16-byte aligned), then
+ * top-k and softmax weights as in moe_topk_softmax: topk_ids int32 [T, k] in
+ * rank order, topk_w fp32 [T, k].  logits_out fp32 [T, E] receives the
+ * logits, or is NULL: the logits then stay on chip (one kernel per batch of
+ * up to 4 tokens, which re-reads the router weights from cache), which
+ * needs 2*H + 4*E + 3328 <= 65536 bytes of LDS for a one-token batch (else
+ * MOE_ERR_UNSUPPORTED).  Both forms select the same experts from the same
+ * fp32 logits below 256 tokens; from 256 tokens with logits_out the logits
+ * come from the matrix cores (same contract, possibly other last bits).
+ * Source: the fused top-k router of "[Model] Add Flint (RecursiveSI/flint)",
+ * section "What happened"; 6 of 256 routed experts per token in the
+ * architecture table of "Recursive Flint: 40B Local Coding Model,
+ * Benchmarks", section "What is Recursive Flint?". */
 int moe_route(const uint16_t* x, const float* w_router, int T, int H, int E, int k,
               float* logits_out, int32_t* topk_ids, float* topk_w, void* stream);
 
-/* Top-k and softmax weights from given fp32 logits [T, E]: ids ranked by
- * (larger logit, lower index); w = exp(l - l_max) / sum over the selection.
- * 1 <= k <= min(E, 8). */
+/* Top-k and softmax weights from given fp32 logits [T, E] (device): ids
+ * int32 [T, k] ranked by (larger logit, lower index); topk_w fp32 [T, k] =
+ * exp(l - l_max) / sum over the selection, so each row sums to 1.
+ * 1 <= k <= min(E, 8), E <= 1024.  NaN logits rank below every number and
+ * ties go to the lower index, so the k ids are always distinct and in
+ * [0, E).  Source: the fused top-k router of "[Model] Add Flint
+ * (RecursiveSI/flint)", section "What happened" (routing as the first of the
+ * layer's steps); top-6 of 256 in "Recursive Flint: 40B Local Coding Model,
+ * Benchmarks", section "What is Recursive Flint?". */
 int moe_topk_softmax(const float* logits, int T, int E, int k,
                      int32_t* topk_ids, float* topk_w, void* stream);
 
@@ -166,7 +186,25 @@ int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* top
                 const float* out_shared, const uint16_t* residual,
                 int T, int k, int H, uint16_t* y, float* y_f32, void* stream);
 
-/* Whole layer for decode-sized batches (1 <= T <= 64 takes the fused path;
+/* Normalisation between chained layers: x[t] = bf16(r[t] / sqrt(mean_h
+ * r[t, h]^2 + eps)) for r, x bf16 [T, H] (device, 16-byte aligned; x may
+ * equal r), H a multiple of 64, eps finite and >= 0.  Squares are summed in
+ * fp32 in a fixed order; each element is divided by the fp32 root and
+ * rounded once (nearest, ties to even).  The pages chain 47 MoE layers
+ * ("Recursive Flint: 40B Local Coding Model, Benchmarks", section "What is
+ * Recursive Flint?") but do not describe the norms between them: this
+ * gain-free RMS normalisation is the stand-in that keeps a chained decode
+ * step in range while every layer's routing depends on the layer before. */
+int moe_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, void* stream);
+
+/* Whole layer for decode-sized batches.  Source: the mixture-of-experts
+ * layer of "Recursive Flint: 40B Local Coding Model, Benchmarks" (section
+ * "What is Recursive Flint?": 256 routed experts, 6 per token, one shared
+ * expert) with the always-on shared expert of "Recursive Flint: 125 tok/s on
+ * an M4 Pro, measured where it matters least" (table under "What actually
+ * shipped"), run as the small-batch fused router + expert-indexed GEMV
+ * kernels of "[Model] Add Flint (RecursiveSI/flint)", section "What
+ * happened".  (1 <= T <= 64 takes the fused path;
  * larger T is composed from the calls above): router, top-k, routed and
  * shared SwiGLU experts on 4-bit weights, combine.  Same numerics as
  * composing moe_route, moe_permute, moe_grouped_w4a16_ffn and moe_combine;

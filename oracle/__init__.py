@@ -47,4 +47,6 @@ from .moe import (  # noqa: F401
     grouped_ffn,
     combine,
     moe_layer,
+    rms_norm,
+    chain_layer,
 )

@@ -33,7 +33,7 @@ Readings taken where the pages are silent:
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, dequant_matrix, rne_bf16
+from .formats import bf16_bits_to_f64, dequant_matrix, f64_to_bf16_bits, rne_bf16
 
 
 def router_logits(x_bits, w_router):
@@ -168,3 +168,25 @@ def moe_layer(layer, x_bits, residual_bits=None, logits=None, tokens=None):
     y = combine(o_pairs, w, o_shared, residual_bits)
     return {"logits": logits, "ids": ids, "w": w, "o_pairs": o_pairs,
             "o_shared": o_shared, "y": y, "y_bf16": rne_bf16(y)}
+
+
+def rms_norm(r_bits, eps):
+    """The normalisation that feeds one chained layer from the residual stream.
+
+    The pages chain 47 MoE layers ("Recursive Flint: 40B Local Coding Model,
+    Benchmarks", section "What is Recursive Flint?") but describe none of the
+    norms between them.  Reading taken: x = r / sqrt(mean_h(r^2) + eps), no
+    learned gain, computed exactly and rounded once to bfloat16 (returned as
+    bit patterns).
+    """
+    r = bf16_bits_to_f64(r_bits)
+    ms = np.mean(r * r, axis=-1, keepdims=True)
+    return f64_to_bf16_bits(rne_bf16(r / np.sqrt(ms + eps)))
+
+
+def chain_layer(layer, r_bits, eps, logits=None):
+    """One layer of the chained decode step: x = rms_norm(r), then the MoE
+    layer with the residual r (its bf16 output is the next residual).
+    Returns (x_bits, the moe_layer result dict)."""
+    x_bits = rms_norm(r_bits, eps)
+    return x_bits, moe_layer(layer, x_bits, residual_bits=r_bits, logits=logits)

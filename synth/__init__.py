@@ -17,6 +17,15 @@ Value recipes (no trained weights exist here; these stand in for them):
                   over the 16 e4m3 codes 0x30..0x3F (values in [0.5, 2));
                   tensor scale ~ U(0.004, 0.008) per (expert, matrix)
   INT4 group 64   codes uniform; fp16 scale ~ U(0.005, 0.02); zero U{0..15}
+  full-range scales (scale_range="full", for parity cases that cover the
+                  whole of both scale formats):
+                  NVFP4 block scales uniform over all 254 non-NaN e4m3 codes
+                  (both signs, subnormals, up to 448) with the tensor scale
+                  divided by 86 (the RMS of those 254 values is about 86
+                  times that of the codes 0x30..0x3F), so the weight RMS
+                  stays near 1/sqrt(H); INT4 fp16 scales with a random sign,
+                  10% of them fp16 subnormals U(2**-24, 2**-14), 5% zeros
+                  (signed), the rest U(0.005, 0.02)
   routing logits  "uniform": fp32 ~ U(0, 1) i.i.d.;
                   "zipf": log p(rank(e)) + Gumbel(0, 1), p(r) ~ r**-s over
                   a seeded permutation of the experts (Gumbel-top-k draws k
@@ -43,41 +52,58 @@ def _gen(device, *keys):
     return g
 
 
-def make_matrix(fmt, num_experts, rows, cols, seed, device="cpu"):
+def make_matrix(fmt, num_experts, rows, cols, seed, device="cpu", scale_range="narrow"):
     """One packed 4-bit matrix stack [num_experts, rows, cols]."""
     if cols % 64 or rows <= 0:
         raise ValueError("cols must be a multiple of 64")
+    if scale_range not in ("narrow", "full"):
+        raise ValueError("scale_range must be 'narrow' or 'full'")
     E = num_experts
     g = _gen(device, seed, 1)
     codes = torch.randint(0, 256, (E, rows, cols // 2), dtype=torch.uint8, device=device, generator=g)
     if fmt == FMT_NVFP4:
-        scales = torch.randint(0x30, 0x40, (E, rows, cols // 16), dtype=torch.uint8, device=device, generator=g)
+        if scale_range == "full":
+            # 254 codes: 0x00..0x7E and 0x80..0xFE (0x7F and 0xFF are NaN)
+            r = torch.randint(0, 254, (E, rows, cols // 16), dtype=torch.int32, device=device, generator=g)
+            scales = (r + (r >= 127).to(torch.int32)).to(torch.uint8)
+        else:
+            scales = torch.randint(0x30, 0x40, (E, rows, cols // 16), dtype=torch.uint8, device=device, generator=g)
         ts = torch.rand((E,), dtype=torch.float32, device=device, generator=g) * 0.004 + 0.004
+        if scale_range == "full":
+            ts = ts / 86.0
         return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols,
                 "codes": codes, "scales": scales, "zeros": None, "tensor_scale": ts}
     if fmt == FMT_INT4_G64:
-        s = (torch.rand((E, rows, cols // 64), dtype=torch.float32, device=device, generator=g) * 0.015 + 0.005)
-        zeros = torch.randint(0, 16, (E, rows, cols // 64), dtype=torch.uint8, device=device, generator=g)
+        shape = (E, rows, cols // 64)
+        s = (torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 0.015 + 0.005)
+        zeros = torch.randint(0, 16, shape, dtype=torch.uint8, device=device, generator=g)
+        if scale_range == "full":
+            kind = torch.rand(shape, dtype=torch.float32, device=device, generator=g)
+            sub = torch.exp2(torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 10.0 - 24.0)
+            s = torch.where(kind < 0.10, sub, s)
+            s = torch.where((kind >= 0.10) & (kind < 0.15), torch.zeros_like(s), s)
+            sign = torch.randint(0, 2, shape, dtype=torch.int32, device=device, generator=g) * 2 - 1
+            s = s * sign.to(torch.float32)
         return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols,
                 "codes": codes, "scales": s.to(torch.float16), "zeros": zeros, "tensor_scale": None}
     raise ValueError("unknown format %r" % (fmt,))
 
 
-def make_ffn(fmt, num_experts, H, I, seed, device="cpu"):
+def make_ffn(fmt, num_experts, H, I, seed, device="cpu", scale_range="narrow"):
     """gate [I, H], up [I, H], down [H, I] for num_experts experts."""
-    return {"gate": make_matrix(fmt, num_experts, I, H, seed_of(seed, 11), device),
-            "up": make_matrix(fmt, num_experts, I, H, seed_of(seed, 12), device),
-            "down": make_matrix(fmt, num_experts, H, I, seed_of(seed, 13), device)}
+    return {"gate": make_matrix(fmt, num_experts, I, H, seed_of(seed, 11), device, scale_range),
+            "up": make_matrix(fmt, num_experts, I, H, seed_of(seed, 12), device, scale_range),
+            "down": make_matrix(fmt, num_experts, H, I, seed_of(seed, 13), device, scale_range)}
 
 
-def make_layer(fmt, H, I, E, k, seed, device="cpu", shared=True, I_shared=None):
+def make_layer(fmt, H, I, E, k, seed, device="cpu", shared=True, I_shared=None, scale_range="narrow"):
     """Router, routed experts and (optionally) the shared expert of one layer."""
     g = _gen(device, seed, 2)
     w_router = torch.randn((E, H), dtype=torch.float32, device=device, generator=g) * 0.02
     return {"fmt": fmt, "H": H, "I": I, "E": E, "k": k,
             "w_router": w_router,
-            "experts": make_ffn(fmt, E, H, I, seed_of(seed, 3), device),
-            "shared": make_ffn(fmt, 1, H, I_shared or I, seed_of(seed, 4), device) if shared else None}
+            "experts": make_ffn(fmt, E, H, I, seed_of(seed, 3), device, scale_range),
+            "shared": make_ffn(fmt, 1, H, I_shared or I, seed_of(seed, 4), device, scale_range) if shared else None}
 
 
 def make_tokens(T, H, seed, device="cpu"):

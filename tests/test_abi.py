@@ -64,6 +64,18 @@ def test_route_validation():
     expect(uns, moe.moe_topk_softmax, FAKE, 4, 2048, 6, FAKE, FAKE)
 
 
+def test_route_logits_out_is_optional():
+    """logits_out may be NULL (the logits then stay on chip); shapes whose
+    one-token batch does not fit 64 KB of LDS are rejected on the host."""
+    uns = moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_route(FAKE, FAKE, 0, 2048, 256, 6, None, FAKE, FAKE) == 0
+    # 2*H + 4*E + 3328 > 65536: H = 30720, E = 1024
+    msg = expect(uns, moe.moe_route, FAKE, FAKE, 4, 30720, 1024, 6, None, FAKE, FAKE)
+    assert "logits_out" in msg
+    # the same shape with a logits buffer is accepted (T = 0: nothing is launched)
+    assert moe.moe_route(FAKE, FAKE, 0, 30720, 1024, 6, FAKE, FAKE, FAKE) == 0
+
+
 def test_zero_tokens_is_a_noop_without_touching_the_gpu():
     assert moe.moe_topk_softmax(FAKE, 0, 32, 6, FAKE, FAKE) == 0
     assert moe.moe_route(FAKE, FAKE, 0, 256, 32, 6, FAKE, FAKE, FAKE) == 0

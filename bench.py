@@ -1,23 +1,34 @@
 """Benchmark of the W4A16 MoE layer on one MI355X.
 
-Default workload: one Flint-shaped MoE decode layer at batch 1 (hidden 2048,
-256 experts top-6 + 1 shared expert, expert inter 768, NVFP4 W4A16 weights,
-bf16 activations).  One step = one moe_layer_decode call on one token: router
-GEMV, top-k + softmax, expert grouping, gate/up + SwiGLU, down projection,
-shared expert and combine.  Steps rotate over independently seeded weight
-copies (more than twice the size of the on-die caches) and fresh tokens, so
-weights stream from HBM; K steps are captured in one HIP graph and replayed.
+Default (``--workload all``): the headline is one Flint-shaped MoE decode
+layer at batch 1 (hidden 2048, 256 experts top-6 + 1 shared expert, expert
+inter 768, NVFP4 W4A16 weights, bf16 activations).  One step = one
+moe_layer_decode call on one token: router GEMV, top-k + softmax, expert
+grouping, gate/up + SwiGLU, down projection, shared expert and combine.
+The same JSON line carries a ``sweep`` object with the rest of the metric:
+decode at 1/4/16/64 tokens in both weight formats, the 47-layer batch-8
+chained decode step, and the 4096-token Zipf(1.1) prefill in both formats,
+each with its roofline fraction and a short timing of the float64 CPU
+oracle on a bounded sample of the same workload.
 
-Other workloads (--workload): decode batch sweep (decode_T4, decode_T16,
-decode_T64, with --fmt int4), the 47-layer batch-8 chain (chain_b8), the
-4096-token prefill (prefill), and hbm_copy: a plain 1 GiB device copy whose
-HBM counter readings calibrate the traffic figures of the others.
+Decode steps rotate over independently seeded weight copies, enough that no
+copy is read again within 512 MB (twice the ~256 MB memory-side cache) of
+weight traffic, and every step gets fresh tokens; the memory-side cache is
+flushed (a 1 GiB copy) before each timed replay.  K steps are captured in
+one HIP graph; one warm replay, then one timed replay between HIP events on
+the launch stream.
 
-Prints ONE JSON line (rank 0).
+Single workloads (``--workload``): decode_b1, decode_T4, decode_T16,
+decode_T64 (with ``--fmt int4`` for the other format), chain_b8, prefill,
+and hbm_copy: a plain 1 GiB device copy whose HBM counter readings calibrate
+the traffic figures.
+
+Prints ONE JSON line.
 """
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -29,6 +40,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s"
+H, I, E, K_TOP = 2048, 768, 256, 6
+CHAIN_LAYERS, CHAIN_T, CHAIN_EPS = 47, 8, 1e-6
+ROTATE_BYTES = 512e6      # no weight copy is read again within this much weight traffic
+MAX_COPIES = 48           # about 33 GB of NVFP4 layer copies
 
 # HBM bytes per measured unit (one layer call; the prefill's grouped FFN) from two rocprofv3
 # --pmc runs of the same workload with the current kernels: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
@@ -46,257 +62,247 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_b1")
+    p.add_argument("--workload", default="all")
     p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4"])
-    p.add_argument("--copies", type=int, default=8, help="independently seeded weight copies to rotate over")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle leg")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the headline's CPU oracle leg")
+    p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-graph", action="store_true")
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import bit_weight_only_moe_amd as moe
-    import synth
+def host_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return len(os.sched_getaffinity(0)), blas
 
-    dev = "cuda"
-    fmt = synth.FMT_NAMES[args.fmt]
-    workload = args.workload
-    if workload == "prefill":
-        return bench_prefill(args, fmt)
-    if workload == "chain_b8":
-        return bench_chain(args, fmt)
-    if workload == "hbm_copy":
-        return bench_copy(args)
-    T = {"decode_b1": 1, "decode_T4": 4, "decode_T16": 16, "decode_T64": 64}.get(workload)
-    if T is None:
-        print("unknown workload %s" % workload, file=sys.stderr)
-        sys.exit(2)
-    H, I, E, k = 2048, 768, 256, 6
-    R = max(1, args.copies)
-    K, W = args.steps, args.warmup
 
-    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(1, r), dev) for r in range(R)]
-    Ls = [moe.Layer(l) for l in layers]
+def cpu_entry(value, unit, sample):
+    cores, blas = host_cores()
+    return {"value": value, "unit": unit, "cores": cores, "blas_threads": blas, "kind": "oracle",
+            "sample": sample + "; float64 numpy oracle as it stands (a correctness reference, not a tuned CPU MoE)"}
+
+
+class Ctx:
+    def __init__(self, args):
+        import torch
+        import bit_weight_only_moe_amd as moe
+        import synth
+        self.args, self.torch, self.moe, self.synth = args, torch, moe, synth
+        self.dev = "cuda"
+        self.stream = torch.cuda.Stream()
+        self._flush = None
+        self._copies = {}
+
+    def flush(self):
+        """Stream 1 GiB through the memory system (evicts the memory-side cache)."""
+        t = self.torch
+        if self._flush is None:
+            self._flush = (t.empty(1 << 29, dtype=t.uint8, device=self.dev),
+                           t.empty(1 << 29, dtype=t.uint8, device=self.dev))
+        with t.cuda.stream(self.stream):
+            self._flush[1].copy_(self._flush[0])
+        t.cuda.synchronize()
+
+    def copies(self, fmt_name, n):
+        """n independently seeded Flint-shaped layers (created once per format, shared by the
+        decode entries and the chain)."""
+        have = self._copies.setdefault(fmt_name, [])
+        fmt = self.synth.FMT_NAMES[fmt_name]
+        while len(have) < n:
+            l = len(have)
+            layer = self.synth.make_layer(fmt, H, I, E, K_TOP, self.synth.seed_of(1, l), self.dev)
+            have.append((layer, self.moe.Layer(layer)))
+        return have[:n]
+
+    def drop(self, fmt_name):
+        self._copies.pop(fmt_name, None)
+        self.torch.cuda.empty_cache()
+
+    def timed(self, body, K, W):
+        """W eager warm-up steps, K steps captured in one graph, one warm replay, a cache
+        flush, then one timed replay between events on the launch stream.  Returns ms."""
+        t, s = self.torch, self.stream
+        with t.cuda.stream(s):
+            for i in range(W):
+                body(i, s)
+        t.cuda.synchronize()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g, stream=s):
+            for i in range(K):
+                body(i, s)
+        g.replay()
+        t.cuda.synchronize()
+        self.flush()
+        ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        with t.cuda.stream(s):
+            ev0.record(s)
+            g.replay()
+            ev1.record(s)
+        t.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+
+def decode_entry(c, fmt_name, T, K, W, cpu_seconds):
+    """K decode steps of one layer at T tokens, rotating over weight copies."""
+    t, moe, synth = c.torch, c.moe, c.synth
+    fmt = synth.FMT_NAMES[fmt_name]
+    eb = synth.expert_bytes(fmt, H, I)
+    exp_touched = E * (1.0 - (1.0 - K_TOP / E) ** T) + 1.0
+    R = int(min(MAX_COPIES, max(K, math.ceil(ROTATE_BYTES / (exp_touched * eb)))))
+    copies = c.copies(fmt_name, R)
     NX = max(K, W, 1)
-    xs = [synth.make_tokens(T, H, synth.seed_of(2, i), dev) for i in range(NX)]
-    ys = [torch.empty_like(x) for x in xs]
-    ids = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NX)]
-    ws_ = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NX)]
-    nws = moe.moe_layer_decode_workspace_size(Ls[0], T)
-    wsb = torch.zeros(nws, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.Stream()
+    xs = [synth.make_tokens(T, H, synth.seed_of(2, T, i), c.dev) for i in range(NX)]
+    ys = [t.empty_like(x) for x in xs]
+    ids = [t.empty((T, K_TOP), dtype=t.int32, device=c.dev) for _ in range(NX)]
+    ws_ = [t.empty((T, K_TOP), dtype=t.float32, device=c.dev) for _ in range(NX)]
+    nws = moe.moe_layer_decode_workspace_size(copies[0][1], T)
+    wsb = t.zeros(nws, dtype=t.uint8, device=c.dev)
 
     def step(i, s):
-        moe.moe_layer_decode(Ls[i % R], xs[i % NX], None, T, ys[i % NX], ids[i % NX], ws_[i % NX], wsb, nws, stream=s)
+        moe.moe_layer_decode(copies[i % R][1], xs[i % NX], None, T, ys[i % NX], ids[i % NX], ws_[i % NX], wsb, nws,
+                             stream=s)
 
-    with torch.cuda.stream(stream):
-        for i in range(W):
-            step(i, stream)
-    torch.cuda.synchronize()
-
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(K):
-                step(i, stream)
-        graph.replay()              # untimed warm replay
-        torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(K):
-                step(i, stream)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    ms_per_step = ms / K
-
-    # algorithmic bytes: distinct touched experts (from the realised routing) + shared expert
-    eb = synth.expert_bytes(fmt, H, I)
-    touched = []
-    for i in range(K):
-        touched.append(len(np.unique(ids[i % NX].cpu().numpy())) + 1)
-    bytes_per_step = eb * float(np.mean(touched))
-    router_bytes = E * H * 4
-    achieved_gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        sample_layers = 2
-        hosts = []
-        for r in range(sample_layers):
-            used = set()
-            for i in range(r, min(NX, 64), R):
-                used |= set(ids[i].cpu().numpy().ravel().tolist())
-            hosts.append(synth.layer_to_numpy(layers[r], experts=used))
-        # the steps r, r+R, ... ran on weight copy r: their experts are in the host copy
-        xs_bits = []
-        for r in range(sample_layers):
-            for i in range(r, min(NX, 64), R):
-                xs_bits.append((r, synth.bits16(xs[i])))
+    ms = c.timed(step, K, W)
+    ms_step = ms / K
+    touched = [len(np.unique(ids[i % NX].cpu().numpy())) + 1 for i in range(K)]
+    bytes_step = eb * float(np.mean(touched))
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    wl = "decode_b1" if T == 1 else "decode_T%d" % T
+    entry = {"workload": "moe_decode_layer T=%d %s H=2048 I=768 E=256 top6+1shared" % (T, fmt_name),
+             "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
+             "weight_copies": R, "distinct_experts_per_step": float(np.mean(touched)),
+             "expert_bytes_per_step": bytes_step, "router_bytes_per_step": E * H * 4,
+             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get((wl, fmt_name)),
+                          "kernel": "moe_layer_decode (one layer call: %s), events on the launch stream"
+                                    % ("k_layer_route_shared + k_layer_gateup + k_layer_down_t1" if T == 1 else
+                                       "k_layer_route_shared + k_layer_gateup + k_layer_down_combine"),
+                          "bytes": "expert weights of the distinct touched experts + shared expert, per call"},
+             "cpu_baseline": None}
+    if cpu_seconds > 0:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            blas_threads = 1
+        # a few of the timed steps (step i ran on weight copy i % R); host copies of the experts
+        # that the GPU or the oracle routes them to are made before the clock starts
+        steps = list(range(min(NX, 8 if T <= 16 else 2)))
+        need = {}
+        for i in steps:
+            r = i % R
+            xb = synth.bits16(xs[i])
+            _, oid, _ = oracle.route(xb, copies[r][0]["w_router"].cpu().numpy(), K_TOP)
+            need.setdefault(r, set()).update(ids[i].cpu().numpy().ravel().tolist() + oid.ravel().tolist())
+        hosts = {r: synth.layer_to_numpy(copies[r][0], experts=ex) for r, ex in need.items()}
+        xbits = {i: synth.bits16(xs[i]) for i in steps}
         t0 = time.perf_counter()
-        n_tok = 0
-        j = 0
-        while time.perf_counter() - t0 < args.cpu_seconds:
-            r, xbits = xs_bits[j % len(xs_bits)]
-            oracle.moe_layer(hosts[r], xbits)
-            n_tok += xbits.shape[0]
-            j += 1
+        calls = 0
+        while True:
+            i = steps[calls % len(steps)]
+            oracle.moe_layer(hosts[i % R], xbits[i])
+            calls += 1
+            if time.perf_counter() - t0 >= cpu_seconds or calls >= 64:
+                break
         el = time.perf_counter() - t0
-        cpu = {"value": n_tok / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-               "sample": "%d layer calls of the same workload (T=%d, %s, %d of %d weight copies), "
-                         "%.1f s of float64 numpy oracle incl. dequantisation of the touched experts"
-                         % (j, T, args.fmt, sample_layers, R, el)}
-
-    out = {
-        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
-        "value": T * K / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "w4(%s)/bf16 act/fp32 acc" % args.fmt,
-        "data": "synthetic",
-        "config": {"workload": "moe_decode_layer T=%d %s H=2048 I=768 E=256 top6+1shared" % (T, args.fmt),
-                   "tokens_per_step": T, "weight_copies": R, "graph": graph is not None,
-                   "expert_bytes_per_step": bytes_per_step, "router_bytes_per_step": router_bytes,
-                   "distinct_experts_per_step": float(np.mean(touched))},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get((workload, args.fmt)),
-                     "kernel": "moe_layer_decode: k_layer_route_shared + k_layer_gateup + %s "
-                               "(one layer call, events on the launch stream)"
-                               % ("k_layer_down_t1" if T == 1 else "k_layer_down_combine"),
-                     "bytes": "expert weights of the distinct touched experts + shared expert, per call"},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out))
+        entry["cpu_baseline"] = cpu_entry(calls * T / el, "tokens/s",
+                                          "%d layer calls of this workload (T=%d, %s; %d distinct steps), %.1f s "
+                                          "incl. dequantisation of the touched experts" % (calls, T, fmt_name,
+                                                                                          len(steps), el))
+    return entry
 
 
-def timed_graph(torch, stream, body, K, W, use_graph=True):
-    """Warm up W eager steps, capture K steps in one graph, time one replay
-    (or, without a graph, time K eager steps)."""
-    with torch.cuda.stream(stream):
-        for i in range(W):
-            body(i, stream)
-    torch.cuda.synchronize()
-    graph = None
-    if use_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(K):
-                body(i, stream)
-        graph.replay()
-        torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(K):
-                body(i, stream)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1)
+def chain_entry(c, fmt_name, K, W, cpu_seconds):
+    """One decode step through 47 chained layers at batch 8: r_0 = tokens; per layer
+    x_l = rms_norm(r_l), r_{l+1} = moe_layer_decode(x_l, residual = r_l), so every layer's
+    routing depends on the layer before."""
+    t, moe, synth = c.torch, c.moe, c.synth
+    fmt = synth.FMT_NAMES[fmt_name]
+    NL, T = CHAIN_LAYERS, CHAIN_T
+    layers = c.copies(fmt_name, NL)
+    NX = max(K, W, 1)
+    r0 = [synth.make_tokens(T, H, synth.seed_of(4, i), c.dev) for i in range(NX)]
+    rs = [t.empty((T, H), dtype=t.bfloat16, device=c.dev) for _ in range(NL)]
+    xn = t.empty((T, H), dtype=t.bfloat16, device=c.dev)
+    ids = [t.empty((T, K_TOP), dtype=t.int32, device=c.dev) for _ in range(NL)]
+    ws_ = [t.empty((T, K_TOP), dtype=t.float32, device=c.dev) for _ in range(NL)]
+    nws = moe.moe_layer_decode_workspace_size(layers[0][1], T)
+    wsb = t.zeros(nws, dtype=t.uint8, device=c.dev)
+
+    def step(i, s):
+        r = r0[i % NX]
+        for l in range(NL):
+            moe.moe_rms_norm(r, T, H, CHAIN_EPS, xn, stream=s)
+            moe.moe_layer_decode(layers[l][1], xn, r, T, rs[l], ids[l], ws_[l], wsb, nws, stream=s)
+            r = rs[l]
+
+    ms = c.timed(step, K, W)
+    ms_step = ms / K
+    eb = synth.expert_bytes(fmt, H, I)
+    bytes_step = sum((len(np.unique(ids[l].cpu().numpy())) + 1) * eb for l in range(NL))
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    entry = {"workload": "moe_decode_chain 47 layers T=8 %s H=2048 I=768 E=256 top6+1shared, rms-normalised "
+                         "residual stream between layers" % fmt_name,
+             "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
+             "expert_bytes_per_step": bytes_step, "resident_weight_bytes": NL * (E + 1) * eb,
+             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                          "kernel": "47 x (k_rms_norm + moe_layer_decode), one step, events on the launch stream"},
+             "cpu_baseline": None}
+    if cpu_seconds > 0:
+        import oracle
+        # the oracle's own chain from one step's input, layer by layer; each layer's host copy
+        # (the experts the oracle routes to) is made off the clock
+        r = synth.bits16(r0[0])
+        el, nl = 0.0, 0
+        while nl < NL and el < cpu_seconds:
+            L = layers[nl][0]
+            x = oracle.rms_norm(r, CHAIN_EPS)
+            _, oid, _ = oracle.route(x, L["w_router"].cpu().numpy(), K_TOP)
+            host = synth.layer_to_numpy(L, experts=set(oid.ravel().tolist()))
+            t0 = time.perf_counter()
+            _, res = oracle.chain_layer(host, r, CHAIN_EPS)
+            el += time.perf_counter() - t0
+            r = oracle.f64_to_bf16_bits(res["y_bf16"])
+            nl += 1
+        step_s = el / nl * NL
+        entry["cpu_baseline"] = cpu_entry(T / step_s, "tokens/s",
+                                          "%d of the 47 chained layers at T=8 (%s), %.1f s of oracle time, scaled "
+                                          "to the 47-layer step" % (nl, fmt_name, el))
+    return entry
 
 
-def bench_copy(args):
-    """A plain device copy of 1 GiB (torch's copy kernel): 1 GiB read + 1 GiB written per step."""
-    import torch
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    src.fill_(1)
-    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
-    stream = torch.cuda.Stream()
-    for _ in range(W):
-        with torch.cuda.stream(stream):
-            dst.copy_(src)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(K):
-            dst.copy_(src)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    gbs = 2.0 * n * K / (ms * 1e-3) / 1e9
-    print(json.dumps({"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
-                      "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,
-                      "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-                      "config": {"workload": "hbm_copy 1 GiB", "bytes_read_per_step": n,
-                                 "bytes_written_per_step": n},
-                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "torch copy"},
-                      "cpu_baseline": None}))
-
-
-def bench_prefill(args, fmt):
+def prefill_entry(c, fmt_name, K, W, cpu_seconds):
     """4096-token prefill of one Flint-shaped layer with Zipf(1.1) expert popularity."""
-    import torch
-    import bit_weight_only_moe_amd as moe
-    import synth
-    dev = "cuda"
-    H, I, E, k, T = 2048, 768, 256, 6, 4096
-    R = max(1, min(args.copies, 2))
-    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
-    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(5, r), dev) for r in range(R)]
-    x = synth.make_tokens(T, H, 5, dev)
-    zl = synth.zipf_logits(T, E, 1.1, 5, dev)
-    n = T * k
-    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sp = torch.empty(n, dtype=torch.int32, device=dev)
-    pp = torch.empty(n, dtype=torch.int32, device=dev)
-    pws_n = moe.moe_permute_workspace_size(T, k, E)
-    pws = torch.empty(pws_n, dtype=torch.uint8, device=dev)
-    out = torch.empty((n, H), dtype=torch.float32, device=dev)
-    out_s = torch.empty((T, H), dtype=torch.float32, device=dev)
-    off_s = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    t, moe, synth = c.torch, c.moe, c.synth
+    fmt = synth.FMT_NAMES[fmt_name]
+    T = 4096
+    R = 2
+    layers = [synth.make_layer(fmt, H, I, E, K_TOP, synth.seed_of(5, r), c.dev) for r in range(R)]
+    x = synth.make_tokens(T, H, 5, c.dev)
+    zl = synth.zipf_logits(T, E, 1.1, 5, c.dev)
+    n = T * K_TOP
+    lg = t.empty((T, E), dtype=t.float32, device=c.dev)
+    ids = t.empty((T, K_TOP), dtype=t.int32, device=c.dev)
+    w = t.empty((T, K_TOP), dtype=t.float32, device=c.dev)
+    counts = t.empty(E, dtype=t.int32, device=c.dev)
+    offsets = t.empty(E + 1, dtype=t.int32, device=c.dev)
+    sp = t.empty(n, dtype=t.int32, device=c.dev)
+    pp = t.empty(n, dtype=t.int32, device=c.dev)
+    pws_n = moe.moe_permute_workspace_size(T, K_TOP, E)
+    pws = t.empty(pws_n, dtype=t.uint8, device=c.dev)
+    out = t.empty((n, H), dtype=t.float32, device=c.dev)
+    out_s = t.empty((T, H), dtype=t.float32, device=c.dev)
+    off_s = t.tensor([0, T], dtype=t.int32, device=c.dev)
     gws_n = max(moe.moe_grouped_ffn_workspace_size(E, H, I, n), moe.moe_grouped_ffn_workspace_size(1, H, I, T))
-    gws = torch.empty(gws_n, dtype=torch.uint8, device=dev)
-    y = torch.empty_like(x)
+    gws = t.empty(gws_n, dtype=t.uint8, device=c.dev)
+    gws_s = t.empty(gws_n, dtype=t.uint8, device=c.dev)
+    y = t.empty_like(x)
     f_routed = [moe.ffn_weights(l["experts"]) for l in layers]
     f_shared = [moe.ffn_weights(l["shared"]) for l in layers]
-
-    # The shared expert needs no routing: its grouped FFN runs on a side stream
-    # (own workspace), forked after the top-k, alongside the permute kernels,
-    # which leave most of the chip idle, and the start of the routed FFN; both
-    # join before the combine.  (Forked before the router it slows the router
-    # about as much as it gains; forked before the top-k it slows the top-k.)
-    side = torch.cuda.Stream()
-    gws_s = torch.empty(gws_n, dtype=torch.uint8, device=dev)
+    # The shared expert needs no routing: its grouped FFN runs on a side stream (own
+    # workspace), forked after the top-k, alongside the permute kernels, which leave most
+    # of the chip idle, and the start of the routed FFN; both join before the combine.
+    side = t.cuda.Stream()
 
     def shared_ffn(i, s):
         side.wait_stream(s)
@@ -304,92 +310,153 @@ def bench_prefill(args, fmt):
                                   gws_n, stream=side)
 
     def routed_ffn(i, s):
-        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, k, offsets, n, out, moe.MOE_MODE_AUTO, gws,
+        moe.moe_grouped_w4a16_ffn(f_routed[i % R], E, H, I, x, sp, K_TOP, offsets, n, out, moe.MOE_MODE_AUTO, gws,
                                   gws_n, stream=s)
 
     def step(i, s):
         L = layers[i % R]
-        moe.moe_route(x, L["w_router"], T, H, E, k, lg, ids, w, stream=s)   # router GEMM (timed; skewed logits route)
-        moe.moe_topk_softmax(zl, T, E, k, ids, w, stream=s)
+        moe.moe_route(x, L["w_router"], T, H, E, K_TOP, lg, ids, w, stream=s)  # router GEMM (timed)
+        moe.moe_topk_softmax(zl, T, E, K_TOP, ids, w, stream=s)             # the skewed logits route
         shared_ffn(i, s)
-        moe.moe_permute(ids, T, k, E, counts, offsets, sp, pp, None, None, 0, pws, pws_n, stream=s)
+        moe.moe_permute(ids, T, K_TOP, E, counts, offsets, sp, pp, None, None, 0, pws, pws_n, stream=s)
         routed_ffn(i, s)
         s.wait_stream(side)
-        moe.moe_combine(out, pp, w, out_s, x, T, k, H, y, stream=s)
+        moe.moe_combine(out, pp, w, out_s, x, T, K_TOP, H, y, stream=s)
 
     def ffn_pair(i, s):
         shared_ffn(i, s)
         routed_ffn(i, s)
         s.wait_stream(side)
 
-    stream = torch.cuda.Stream()
-    ms = timed_graph(torch, stream, step, K, W, not args.no_graph)
-    # the grouped FFN alone (routed + shared), timed the same way
-    ms_ffn = timed_graph(torch, stream, ffn_pair, K, W, not args.no_graph)
+    ms = c.timed(step, K, W)
+    ms_ffn = c.timed(ffn_pair, K, W)
     flops = 6.0 * (n + T) * H * I
-    c = counts.cpu().numpy()
-    out_line = {
-        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
-        "value": flops / (ms / K * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "w4(%s)/bf16 mfma/fp32 acc" % args.fmt, "data": "synthetic",
-        "config": {"workload": "moe_prefill T=4096 %s H=2048 I=768 E=256 top6+1shared zipf1.1" % args.fmt,
-                   "expert_gflop": flops / 1e9, "tokens_per_s": T * K / (ms * 1e-3),
-                   "max_rows_per_expert": int(c.max()), "min_rows_per_expert": int(c.min()), "weight_copies": R},
-        "roofline": {"bound": "mfma", "achieved": flops / (ms_ffn / K * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": flops / (ms_ffn / K * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": TRAFFIC_BYTES.get(("prefill", args.fmt)),
-                     "kernel": "moe_grouped_w4a16_ffn routed + shared: k_tile_table, %s gate/up, %s down"
-                               % (("k_mfma_bl",) * 2 if fmt == 1 else ("k_mfma_bd",) * 2)},
-        "cpu_baseline": None,
-    }
-    print(json.dumps(out_line))
+    cnt = counts.cpu().numpy()
+    ffn_tf = flops / (ms_ffn / K * 1e-3) / 1e12
+    entry = {"workload": "moe_prefill T=4096 %s H=2048 I=768 E=256 top6+1shared zipf1.1" % fmt_name,
+             "tflops": flops / (ms / K * 1e-3) / 1e12, "tokens_per_s": T * K / (ms * 1e-3),
+             "ms_per_step": ms / K, "ffn_ms": ms_ffn / K, "steps": K, "warmup": W, "expert_gflop": flops / 1e9,
+             "max_rows_per_expert": int(cnt.max()), "min_rows_per_expert": int(cnt.min()),
+             "roofline": {"bound": "mfma", "achieved": ffn_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": ffn_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": TRAFFIC_BYTES.get(("prefill", fmt_name)),
+                          "kernel": "moe_grouped_w4a16_ffn routed + shared (%s gate/up and down), events on the "
+                                    "launch stream" % ("k_mfma_bl" if fmt == 1 else "k_mfma_bd")},
+             "cpu_baseline": None}
+    if cpu_seconds > 0:
+        import oracle
+        lg_np = zl.cpu().numpy()
+        ids_np = oracle.topk_select(lg_np.astype(np.float64), K_TOP)
+        xb = synth.bits16(x)
+        n_tok = 32
+        toks = np.arange(n_tok)
+        host = synth.layer_to_numpy(layers[0], experts=set(ids_np[toks].ravel().tolist()))
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.moe_layer(host, xb, residual_bits=xb, logits=lg_np, tokens=toks)
+            done += 1
+            if time.perf_counter() - t0 >= cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        f = 6.0 * (n_tok * K_TOP + n_tok) * H * I * done
+        entry["cpu_baseline"] = cpu_entry(f / el / 1e12, "TFLOP/s",
+                                          "%d oracle runs over the first 32 of the 4096 Zipf-routed tokens (%s), "
+                                          "%.1f s incl. dequantisation of their experts" % (done, fmt_name, el))
+    return entry
 
 
-def bench_chain(args, fmt):
-    """One decode step through 47 chained MoE layers at batch 8.
+def copy_line(c, args):
+    """A plain device copy of 1 GiB (torch's copy kernel): 1 GiB read + 1 GiB written per step."""
+    t = c.torch
+    n = 1 << 30
+    src = t.empty(n, dtype=t.uint8, device="cuda")
+    dst = t.empty_like(src)
+    src.fill_(1)
+    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    for _ in range(W):
+        with t.cuda.stream(c.stream):
+            dst.copy_(src)
+    t.cuda.synchronize()
+    ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+    with t.cuda.stream(c.stream):
+        ev0.record(c.stream)
+        for _ in range(K):
+            dst.copy_(src)
+        ev1.record(c.stream)
+    t.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    gbs = 2.0 * n * K / (ms * 1e-3) / 1e9
+    return {"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+            "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "hbm_copy 1 GiB", "bytes_read_per_step": n, "bytes_written_per_step": n},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "torch copy"},
+            "cpu_baseline": None}
 
-    Layer l adds its MoE output to the residual stream r: r_{l+1} = r_l + MoE_l(x_l).
-    In the model x_l is the normalised residual; the normalisation is outside the
-    MoE layer, so each layer reads a seeded unit-scale stand-in x_l and the chain
-    runs through the residual (without it, SwiGLU's roughly quadratic growth would
-    overflow bf16 within a few layers)."""
-    import torch
-    import bit_weight_only_moe_amd as moe
-    import synth
-    dev = "cuda"
-    H, I, E, k, T, NL = 2048, 768, 256, 6, 8, 47
-    K, W = max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
-    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(4, l), dev) for l in range(NL)]
-    Ls = [moe.Layer(l) for l in layers]
-    xin = [synth.make_tokens(T, H, synth.seed_of(5, l), dev) for l in range(NL)]
-    rs = [synth.make_tokens(T, H, 4, dev)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
-    ids = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NL)]
-    ws_ = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NL)]
-    nws = moe.moe_layer_decode_workspace_size(Ls[0], T)
-    wsb = torch.zeros(nws, dtype=torch.uint8, device=dev)
 
-    def step(i, s):
-        for l in range(NL):
-            moe.moe_layer_decode(Ls[l], xin[l], rs[l], T, rs[l + 1], ids[l], ws_[l], wsb, nws, stream=s)
+def line_from(entry, fmt_name, value_key, unit, K, W):
+    cfg = {k: v for k, v in entry.items() if k not in ("roofline", "cpu_baseline", "ms_per_step", "steps", "warmup")}
+    return {"metric": METRIC, "value": entry[value_key], "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": entry["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "w4(%s)/bf16 act/fp32 acc" % fmt_name, "data": "synthetic", "config": cfg,
+            "roofline": entry["roofline"], "cpu_baseline": entry["cpu_baseline"]}
 
-    stream = torch.cuda.Stream()
-    ms = timed_graph(torch, stream, step, K, W)
-    eb = synth.expert_bytes(fmt, H, I)
-    bytes_step = sum((len(np.unique(ids[l].cpu().numpy())) + 1) * eb for l in range(NL))
-    gbs = bytes_step / (ms / K * 1e-3) / 1e9
-    out_line = {
-        "metric": "MoE decode tokens/s and weight HBM GB/s (% of peak), batch 1-64; prefill TFLOP/s",
-        "value": T * K / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "w4(%s)/bf16 act/fp32 acc" % args.fmt, "data": "synthetic",
-        "config": {"workload": "moe_decode_chain 47 layers T=8 %s H=2048 I=768 E=256 top6+1shared" % args.fmt,
-                   "expert_bytes_per_step": bytes_step, "resident_weight_bytes": NL * (E + 1) * eb},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": "47 x moe_layer_decode"},
-        "cpu_baseline": None,
-    }
-    print(json.dumps(out_line))
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    c = Ctx(args)
+    K, W = max(1, args.steps), max(0, args.warmup)
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    scpu = 0.0 if args.no_cpu_baseline else args.sweep_cpu_seconds
+    wl = args.workload
+    decode_T = {"decode_b1": 1, "decode_T4": 4, "decode_T16": 16, "decode_T64": 64}
+    Kc, Wc = max(1, min(K, 10)), max(1, min(W, 3))       # the chain and prefill steps are long
+    if wl == "hbm_copy":
+        print(json.dumps(copy_line(c, args)))
+        return
+    if wl in decode_T:
+        e = decode_entry(c, args.fmt, decode_T[wl], K, W, cpu)
+        print(json.dumps(line_from(e, args.fmt, "tokens_per_s", "tokens/s", K, W)))
+        return
+    if wl == "chain_b8":
+        e = chain_entry(c, args.fmt, Kc, Wc, cpu)
+        print(json.dumps(line_from(e, args.fmt, "tokens_per_s", "tokens/s", Kc, Wc)))
+        return
+    if wl == "prefill":
+        e = prefill_entry(c, args.fmt, Kc, Wc, cpu)
+        out = line_from(e, args.fmt, "tflops", "TFLOP/s", Kc, Wc)
+        out["dtype"] = "w4(%s)/bf16 mfma/fp32 acc" % args.fmt
+        print(json.dumps(out))
+        return
+    if wl != "all":
+        print("unknown workload %s" % wl, file=sys.stderr)
+        sys.exit(2)
+    # the headline, then the rest of the metric
+    head = decode_entry(c, "nvfp4", 1, K, W, cpu)
+    sweep = {}
+    t_start = time.perf_counter()
+    for fmt_name in ("nvfp4", "int4"):
+        for T in (1, 4, 16, 64):
+            if fmt_name == "nvfp4" and T == 1:
+                continue
+            sweep["decode_T%d_%s" % (T, fmt_name)] = decode_entry(c, fmt_name, T, K, W, scpu)
+            print("[bench] decode T=%d %s done (%.0f s)" % (T, fmt_name, time.perf_counter() - t_start),
+                  file=sys.stderr, flush=True)
+        if fmt_name == "nvfp4":
+            sweep["chain_b8_nvfp4"] = chain_entry(c, "nvfp4", Kc, Wc, scpu)
+            print("[bench] chain done (%.0f s)" % (time.perf_counter() - t_start), file=sys.stderr, flush=True)
+        c.drop(fmt_name)
+        sweep["prefill_%s" % fmt_name] = prefill_entry(c, fmt_name, Kc, Wc, scpu)
+        c.torch.cuda.empty_cache()
+        print("[bench] prefill %s done (%.0f s)" % (fmt_name, time.perf_counter() - t_start), file=sys.stderr,
+              flush=True)
+    out = line_from(head, "nvfp4", "tokens_per_s", "tokens/s", K, W)
+    out["sweep"] = sweep
+    print(json.dumps(out))
 
 
 if __name__ == "__main__":

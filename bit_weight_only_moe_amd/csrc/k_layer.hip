@@ -90,6 +90,7 @@ struct LayerArgs {
   int lpr_h, lpr_i, lpr_is;
   int down_stage_bytes;      // launch 3: LDS bytes of the token staging (16-byte multiple)
   int rows_t1;               // one token: output rows per down block, every unit (0: not used)
+  int sync_slices;           // slice tickets in the workspace (cleared by launch 1)
 };
 
 
@@ -263,6 +264,12 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   __shared__ int ticket;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, E = a.E;
+  // The down launch's slice tickets are cleared here (that launch starts after
+  // this one ends), the router tickets by the gate/up launch: every call
+  // leaves its counters at zero, and a call also clears the other launch's
+  // counters, so a call that never finished cannot upset the next one.
+  if (blockIdx.x == 0)
+    for (int q = tid; q < a.sync_slices; q += 256) a.sync[kTicketSlice + 16 * q] = 0;
   if ((int)blockIdx.x >= a.nR) {
     const int b = blockIdx.x - a.nR;
     const int slice = b % a.ss_r, r0 = (b / a.ss_r) * NT;
@@ -461,6 +468,7 @@ __global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_laye
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
   const int unit = blockIdx.x / a.slices_r;
+  if (blockIdx.x == 0 && threadIdx.x <= kMaxBatches) a.sync[16 * threadIdx.x] = 0;  // router tickets
   if (threadIdx.x < kRec) s_rec[threadIdx.x] = a.rec[(size_t)unit * kRec + threadIdx.x];
   __syncthreads();
   const int e = s_rec[0];
@@ -893,6 +901,7 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.lpr_is = a.Is ? std::min(lanes_per_row(a.Is), NT == 1 ? 64 : kLprDownTokens) : 64;
   a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
   a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr);
+  a.sync_slices = (a.H + kRDMin - 1) / kRDMin;
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const bool nv = L->experts.gate.fmt == kFmtNvfp4;
   if (NT == 1)

@@ -28,7 +28,7 @@ EXPORTED = [
     "moe_abi_version", "moe_last_error", "moe_dequant_w4", "moe_route", "moe_topk_softmax",
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_ffn_workspace_size",
     "moe_grouped_w4a16_ffn", "moe_combine", "moe_layer_decode_workspace_size", "moe_layer_decode",
-    "moe_rms_norm",
+    "moe_rms_norm", "moe_layer_decode_noalloc_max_bytes", "moe_layer_decode_noalloc",
 ]
 
 
@@ -74,6 +74,8 @@ def _load():
         "moe_layer_decode_workspace_size": (Z, [ctypes.POINTER(LayerWeights), I]),
         "moe_layer_decode": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, P, Z, S]),
         "moe_rms_norm": (I, [P, I, I, ctypes.c_float, P, S]),
+        "moe_layer_decode_noalloc_max_bytes": (Z, []),
+        "moe_layer_decode_noalloc": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -190,3 +192,13 @@ def moe_layer_decode(layer, x, residual, T, y, ids_out=None, w_out=None, ws=None
 
 def moe_rms_norm(r, T, H, eps, x, stream=None):
     return _check(_lib.moe_rms_norm(_ptr(r), T, H, float(eps), _ptr(x), _stream(stream)))
+
+
+def moe_layer_decode_noalloc_max_bytes():
+    return _lib.moe_layer_decode_noalloc_max_bytes()
+
+
+def moe_layer_decode_noalloc(layer, x, residual, T, y, ids_out=None, w_out=None, stream=None):
+    L = layer if isinstance(layer, Layer) else Layer(layer)
+    return _check(_lib.moe_layer_decode_noalloc(ctypes.byref(L.c), _ptr(x), _ptr(residual), T, _ptr(y),
+                                                _ptr(ids_out), _ptr(w_out), _stream(stream)))

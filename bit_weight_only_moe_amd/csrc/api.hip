@@ -3,9 +3,20 @@
 // so a failing call enqueues nothing.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
+
+// ---- scratch memory for moe_layer_decode_noalloc ------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from module load (zero-filled) until the process ends.  Host code never
+// uses the name `scratch` as an address (on the host it is only a stand-in
+// symbol): each device's address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is passed
+// to kernels.
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -139,6 +150,36 @@ size_t decode_ws(const moe_layer_weights* L, int T, void* base, DecodeWs* d) {
                                            : 0);
   if (d) *d = t;
   return c.used;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch`, or NULL with the error recorded.
+void* scratch_for_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(MOE_ERR_HIP, "moe_layer_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode_noalloc: device %d >= %d", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(MOE_ERR_HIP, "moe_layer_decode_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -333,21 +374,55 @@ size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T) {
   return decode_ws(L, T, nullptr, nullptr);
 }
 
+static int check_decode_args(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
+                             const uint16_t* y, const int32_t* ids_out, const float* w_out, const char* who) {
+  int rc = check_layer(L, who);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", who, T);
+  if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "%s: null x or y", who);
+  if ((ids_out == nullptr) != (w_out == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "%s: ids_out and w_out must both be given or both be NULL", who);
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: x / y / residual must be 16-byte aligned", who);
+  return MOE_OK;
+}
+
+static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
+                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream);
+
 int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T, uint16_t* y,
                      int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_layer(L, "moe_layer_decode");
+  int rc = check_decode_args(L, x, residual, T, y, ids_out, w_out, "moe_layer_decode");
   if (rc) return rc;
-  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: T=%d < 0", T);
-  if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: null x or y");
-  if ((ids_out == nullptr) != (w_out == nullptr))
-    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: ids_out and w_out must both be given or both be NULL");
-  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)))
-    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: x / y / residual must be 16-byte aligned");
   const size_t need = decode_ws(L, T, nullptr, nullptr);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: workspace %zu < %zu bytes or not 256-byte aligned", ws_bytes,
                 need);
   if (T == 0) return MOE_OK;
+  return layer_decode_on(L, x, residual, T, y, ids_out, w_out, ws, stream);
+}
+
+size_t moe_layer_decode_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int moe_layer_decode_noalloc(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
+                             uint16_t* y, int32_t* ids_out, float* w_out, void* stream) {
+  int rc = check_decode_args(L, x, residual, T, y, ids_out, w_out, "moe_layer_decode_noalloc");
+  if (rc) return rc;
+  if (T > kDecodeMaxT)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode_noalloc: T=%d > %d (the fused decode path only)", T,
+                kDecodeMaxT);
+  const size_t need = decode_ws(L, T, nullptr, nullptr);
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode_noalloc: this layer needs %zu bytes of scratch at T=%d, "
+                "more than the static %zu", need, T, kNoallocScratchBytes);
+  if (T == 0) return MOE_OK;
+  void* p = scratch_for_current_device();
+  if (!p) return MOE_ERR_HIP;
+  return layer_decode_on(L, x, residual, T, y, ids_out, w_out, p, stream);
+}
+
+static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
+                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream) {
   DecodeWs d;
   decode_ws(L, T, ws, &d);
   hipStream_t s = as_stream(stream);

@@ -224,6 +224,25 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
                      int T, uint16_t* y, int32_t* ids_out, float* w_out,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same kernels, numerics and
+ * arguments as moe_layer_decode; its scratch memory is a static device array
+ * of moe_layer_decode_noalloc_max_bytes() bytes (8 MiB) that each GPU the
+ * library runs on holds from the first use until the process ends; the call
+ * allocates and frees nothing.  Only the fused path: 0 <= T <= 64, and the
+ * layer's workspace at T (moe_layer_decode_workspace_size) must fit the
+ * array, else MOE_ERR_UNSUPPORTED with nothing enqueued (a Flint-shaped
+ * layer needs about 4.5 MiB at 64 tokens).  The array belongs to the
+ * calling thread's current device, which must be the stream's device.
+ * Every call on one GPU shares that GPU's array and leaves in it the state
+ * the next call expects (ticket counters at zero), so calls that overlap on
+ * one GPU (two streams, two threads) race and must be serialised by the
+ * caller. */
+size_t moe_layer_decode_noalloc_max_bytes(void);
+int moe_layer_decode_noalloc(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual,
+                             int T, uint16_t* y, int32_t* ids_out, float* w_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -135,3 +135,22 @@ def test_layer_decode_validation():
     expect(inv, moe.moe_layer_decode, bad_k, FAKE, None, 8, FAKE, ws=FAKE, ws_bytes=need)
     assert moe.moe_layer_decode(layer, FAKE, None, 0, FAKE, ws=FAKE, ws_bytes=need) == 0
     assert "workspace" in moe.moe_last_error() or moe.moe_last_error() != ""
+
+
+def test_layer_decode_noalloc_validation():
+    """The static-scratch entry point rejects, on the host, what its array
+    cannot hold: more than 64 tokens, or a layer whose workspace exceeds the
+    array (before it touches any device)."""
+    inv, uns = moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED
+    cap = moe.moe_layer_decode_noalloc_max_bytes()
+    assert cap == 8 << 20
+    layer = {"H": 256, "I": 128, "E": 4, "k": 2, "w_router": FAKE, "experts": fake_ffn(), "shared": fake_ffn(E=1)}
+    assert moe.moe_layer_decode_noalloc(layer, FAKE, None, 0, FAKE) == 0
+    expect(uns, moe.moe_layer_decode_noalloc, layer, FAKE, None, 65, FAKE)
+    expect(inv, moe.moe_layer_decode_noalloc, layer, FAKE, None, -1, FAKE)
+    expect(inv, moe.moe_layer_decode_noalloc, layer, FAKE, None, 4, FAKE, ids_out=FAKE, w_out=None)
+    big = {"H": 3840, "I": 512, "E": 1024, "k": 8, "w_router": FAKE, "experts": fake_ffn(E=1024, H=3840, I=512),
+           "shared": fake_ffn(E=1, H=3840, I=512)}
+    assert moe.moe_layer_decode_workspace_size(big, 64) > cap
+    msg = expect(uns, moe.moe_layer_decode_noalloc, big, FAKE, None, 64, FAKE)
+    assert "scratch" in msg

@@ -53,6 +53,17 @@ constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
 
+// Compile-time shapes: GP = H / 32 and IP = I / 32 pieces per gate/up and down
+// row (0: the runtime shape).  Lanes per row as the launcher picks them at
+// runtime: the largest power of two up to a cap that divides the pieces.
+constexpr int lanes_for(int pieces, int cap) {
+  int l = cap;
+  while (l > 1 && pieces % l) l >>= 1;
+  return l;
+}
+constexpr int gate_lpr(int NT, int GP) { return GP ? lanes_for(GP, NT == 1 ? 64 : kLprTokens) : 0; }
+constexpr int down_lpr(int NT, int IP) { return IP ? lanes_for(IP, NT == 1 ? 64 : kLprDownTokens) : 0; }
+
 // Synchronisation words (ints) at the start of the workspace, 64 bytes apart.
 constexpr int kTicketGroup = 0;                         // batches routed
 constexpr int kTicketBatch = 16;                        // + 16 * batch: router blocks of a batch done
@@ -114,15 +125,23 @@ MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, 
 
 // h[r, i] = bf16(silu(gate_e[i] . x_tok(r)) * (up_e[i] . x_tok(r))) for the
 // rows r in [r0, r1) and output rows i in [i0, i1).  tok_of(r): token index.
-template <int FMT, int NT, typename TokOf>
-MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1, int i0, int i1, int H,
+// KP > 0: the rows have KP pieces (H = 32 KP) and LPR lanes share a row, both
+// compile-time, and the block's rows take one iteration of its waves (i1 - i0
+// <= 4 * 64 / LPR): the piece loop, its row and piece indices and the lane
+// reductions are then constants.  KP == 0: the same computation with the
+// runtime shape.
+template <int FMT, int NT, int KP = 0, int LPR = 0, typename TokOf>
+MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1, int i0, int i1, int H_rt,
                          const uint16_t* __restrict__ x, TokOf tok_of, uint16_t* __restrict__ hout, int Iu,
-                         int lpr, uint8_t* smem, int kern) {
+                         int lpr_rt, uint8_t* smem) {
+  constexpr bool FIX = KP > 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int H = FIX ? 32 * KP : H_rt;
+  const int lpr = FIX ? LPR : lpr_rt;
   const int rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
   const int ppl = (H / 32) / lpr;
-  const int iters = (i1 - i0 + 4 * rpw - 1) / (4 * rpw);  // row iterations per wave
-  const int npc = iters * ppl;                            // pieces per lane per matrix
+  const int iters = FIX ? 1 : (i1 - i0 + 4 * rpw - 1) / (4 * rpw);  // row iterations per wave
+  const int npc = iters * ppl;                                       // pieces per lane per matrix
   uint16_t* xs = (uint16_t*)smem;
   float* xsum = (float*)(smem + (size_t)NT * H * sizeof(uint16_t));
   const float tsg = tensor_scale<FMT>(G, e), tsu = tensor_scale<FMT>(U, e);
@@ -148,18 +167,23 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
       for (int q = 0; q < PC; ++q) {
         const int c = c0 + q;
         if (c < npc) {
-          const int i = row0 + 4 * rpw * (c / ppl);
+          const int i = FIX ? row0 : row0 + 4 * rpw * (c / ppl);
           if (i < i1) {
-            const int p = lir + (c % ppl) * lpr;
+            const int p = lir + (FIX ? c : c % ppl) * lpr;
             piece_dot<FMT, NT>(rg[q], p, xs, H, xsum, H / 32, nt, ag);
             piece_dot<FMT, NT>(ru[q], p, xs, H, xsum, H / 32, nt, au);
           }
-          if (c % ppl == ppl - 1) {  // the row's last piece: reduce over its lanes and emit
+          if ((FIX ? c : c % ppl) == ppl - 1) {  // the row's last piece: reduce over its lanes and emit
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               if (t < nt) {
-                ag[t] = group_sum_last_dyn(ag[t], lpr);
-                au[t] = group_sum_last_dyn(au[t], lpr);
+                if (FIX) {
+                  ag[t] = group_sum_last<LPR>(ag[t]);
+                  au[t] = group_sum_last<LPR>(au[t]);
+                } else {
+                  ag[t] = group_sum_last_dyn(ag[t], lpr);
+                  au[t] = group_sum_last_dyn(au[t], lpr);
+                }
               }
             }
             if (i < i1 && lir == lpr - 1) {
@@ -181,14 +205,17 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
 // out[r, n] = down_e[n] . h_r (fp32, unweighted) for rows r in [r0, r1) of
 // `hin` (row stride K) and output rows n in [n0, n1).  Stores with st_dev
 // when `coherent` (another block of the same launch reads them).
-template <int FMT, int NT>
+// KP, LPR as for gateup_rows (K = 32 KP; n1 - n0 <= 4 * 64 / LPR when KP > 0).
+template <int FMT, int NT, int KP = 0, int LPR = 0>
 MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, const uint16_t* __restrict__ hin,
-                       float* __restrict__ out, int lpr, bool coherent, uint8_t* smem) {
+                       float* __restrict__ out, int lpr_rt, bool coherent, uint8_t* smem) {
+  constexpr bool FIX = KP > 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int K = D.cols, H = D.rows;
+  const int K = FIX ? 32 * KP : D.cols, H = D.rows;
+  const int lpr = FIX ? LPR : lpr_rt;
   const int rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
   const int ppl = (K / 32) / lpr;
-  const int iters = (n1 - n0 + 4 * rpw - 1) / (4 * rpw);
+  const int iters = FIX ? 1 : (n1 - n0 + 4 * rpw - 1) / (4 * rpw);
   const int npc = iters * ppl;
   uint16_t* xs = (uint16_t*)smem;
   float* xsum = (float*)(smem + (size_t)NT * K * sizeof(uint16_t));
@@ -200,9 +227,9 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   if (resident) {
 #pragma unroll
     for (int q = 0; q < PC; ++q) {
-      const int n = row0 + 4 * rpw * (q / ppl);
+      const int n = FIX ? row0 : row0 + 4 * rpw * (q / ppl);
       if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
-                                                      lir + (q % ppl) * lpr);
+                                                      lir + (FIX ? q : q % ppl) * lpr);
     }
   }
   for (int rb = r0; rb < r1; rb += NT) {
@@ -228,12 +255,12 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
       for (int q = 0; q < PC; ++q) {
         const int c = c0 + q;
         if (c < npc) {
-          const int n = row0 + 4 * rpw * (c / ppl);
-          if (n < n1) piece_dot<FMT, NT>(rd[q], lir + (c % ppl) * lpr, xs, K, xsum, K / 32, nt, acc);
-          if (c % ppl == ppl - 1) {  // the row's last piece
+          const int n = FIX ? row0 : row0 + 4 * rpw * (c / ppl);
+          if (n < n1) piece_dot<FMT, NT>(rd[q], lir + (FIX ? c : c % ppl) * lpr, xs, K, xsum, K / 32, nt, acc);
+          if ((FIX ? c : c % ppl) == ppl - 1) {  // the row's last piece
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-              if (t < nt) acc[t] = group_sum_last_dyn(acc[t], lpr);
+              if (t < nt) acc[t] = FIX ? group_sum_last<LPR>(acc[t]) : group_sum_last_dyn(acc[t], lpr);
             if (n < n1 && lir == lpr - 1) {
 #pragma unroll
               for (int t = 0; t < NT; ++t) {
@@ -258,7 +285,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
 // block that takes the last router ticket does top-k + softmax for every
 // token and groups the (token, choice) pairs by expert.
 // Blocks [nR, ...): shared expert gate/up, one (row slice, token batch) each.
-template <int FMT, int NT>
+template <int FMT, int NT, int GP, int IP>
 __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int ticket;
@@ -274,8 +301,9 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     const int b = blockIdx.x - a.nR;
     const int slice = b % a.ss_r, r0 = (b / a.ss_r) * NT;
     const int i0 = slice * a.rg, i1 = min(a.Is, i0 + a.rg);
-    gateup_rows<FMT, NT>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x, [](int r) { return r; },
-                         a.h_shared, a.Is, a.lpr_h, smem, 0);
+    gateup_rows<FMT, NT, GP, gate_lpr(NT, GP)>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x,
+                                               [](int r) { return r; },
+                         a.h_shared, a.Is, a.lpr_h, smem);
     return;
   }
   const int nb = a.nR / a.nRe;  // token batches
@@ -463,7 +491,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
 // INT4 with several tokens: bounded to 128 registers (4 waves per SIMD; it
 // fits without spilling, 5 registers under its unbounded allocation, and
 // runs T=16/64 4-6% faster than at 3 waves)
-template <int FMT, int NT>
+template <int FMT, int NT, int GP, int IP>
 __global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_layer_gateup(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
@@ -475,8 +503,8 @@ __global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_laye
   if (e < 0) return;
   const int r0 = s_rec[1];
   const int i0 = (blockIdx.x % a.slices_r) * a.rg, i1 = min(a.I, i0 + a.rg);
-  gateup_rows<FMT, NT>(a.gate, a.up, e, r0, r0 + s_rec[2], i0, i1, a.H, a.x,
-                       [r0](int r) { return s_rec[4 + r - r0]; }, a.h_routed, a.I, a.lpr_h, smem, 1);
+  gateup_rows<FMT, NT, GP, gate_lpr(NT, GP)>(a.gate, a.up, e, r0, r0 + s_rec[2], i0, i1, a.H, a.x,
+                       [r0](int r) { return s_rec[4 + r - r0]; }, a.h_routed, a.I, a.lpr_h, smem);
 }
 
 // ------------------------------------------------------------------ launch 3
@@ -484,7 +512,7 @@ __global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_laye
 // token batches, then the routed records.  fp32 outputs go to the
 // workspace; the last block of each slice combines
 // y = residual + sum_j w_j o_j + o_shared in that fixed order.
-template <int FMT, int NT>
+template <int FMT, int NT, int GP, int IP>
 __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
@@ -511,11 +539,13 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   if (routed) {
     const int e = s_rec[0];
     if (e < 0) return;
-    down_rows<FMT, NT>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed, a.o_routed, a.lpr_i, true,
+    down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed,
+                                             a.o_routed, a.lpr_i, true,
                        smem);
   } else {
     const int r0 = unit * NT;
-    down_rows<FMT, NT>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared, a.lpr_is, true, smem);
+    down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared,
+                                             a.lpr_is, true, smem);
   }
   block_stores_done();
   const int units = s_nact + a.nsb;
@@ -594,7 +624,7 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
 // combine: the results are those of the general launch 3, bit for bit.
 constexpr int kMaxUnitsT1 = 9;   // k <= 8 routed experts + the shared expert
 constexpr int kT1Threads = 256;  // measured: 512 (8 rows per block) the same, 1024 slower
-template <int FMT>
+template <int FMT, int IP>
 __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_e[kMaxUnitsT1];
@@ -616,8 +646,9 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
     s_pp[tid] = 0;
   }
   __syncthreads();
-  const int lpr = a.lpr_i, rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
-  const int ppl = (I / 32) / lpr;
+  constexpr int LPR_C = down_lpr(1, IP);
+  const int lpr = IP ? LPR_C : a.lpr_i, rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
+  const int ppl = IP ? IP / LPR_C : (I / 32) / lpr;
   const int d = wave * rpw + rsub;  // this lane group's row-dot: unit d / R, row n0 + d % R
   const int u = d / R, n = n0 + d % R;
   const bool active = u < nu && n < H;
@@ -662,7 +693,7 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
 #pragma unroll
   for (int q = 0; q < kMaxPcD; ++q)
     if (q < ppl) piece_dot<FMT, 1>(rd[q], lir + q * lpr, xs + (size_t)uc * I, I, xsum + uc * (I / 32), I / 32, 1, acc);
-  acc[0] = group_sum_last_dyn(acc[0], lpr);
+  acc[0] = IP ? group_sum_last<LPR_C>(acc[0]) : group_sum_last_dyn(acc[0], lpr);
   if (active && lir == lpr - 1) s_o[d] = acc[0] * tensor_scale<FMT>(D, e);
   __syncthreads();
   if (tid < R && n0 + tid < H) {
@@ -723,7 +754,7 @@ __global__ void __launch_bounds__(256) k_grouped_gateup(GroupedArgs g) {
   const int32_t* sp = g.sorted_pairs;
   const int k = g.k;
   gateup_rows<FMT, NT>(g.gate, g.up, e, r0, r1, i0, i1, g.H, g.x,
-                       [sp, k](int r) { return sp ? sp[r] / k : r; }, g.h, g.I, g.lpr_h, smem, 1);
+                       [sp, k](int r) { return sp ? sp[r] / k : r; }, g.h, g.I, g.lpr_h, smem);
 }
 
 template <int FMT, int NT>
@@ -834,18 +865,35 @@ static int down_t1_rows(int T, int I, int Is, int k, bool shared) {
   return rows;
 }
 
-template <int FMT, int NT>
+template <int FMT, int NT, int GP, int IP>
 static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_layer_route_shared<FMT, NT>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s, a);
-  hipLaunchKernelGGL((k_layer_gateup<FMT, NT>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
+  hipLaunchKernelGGL((k_layer_route_shared<FMT, NT, GP, IP>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s,
+                     a);
+  hipLaunchKernelGGL((k_layer_gateup<FMT, NT, GP, IP>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
   if (NT == 1 && a.rows_t1 > 0) {
     const int units = a.k + (a.nsb > 0 ? 1 : 0);
     const size_t l1 = (size_t)units * a.I * 2 + (size_t)units * (a.I / 32) * 4;
-    hipLaunchKernelGGL((k_layer_down_t1<FMT>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s, a);
+    hipLaunchKernelGGL((k_layer_down_t1<FMT, IP>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s,
+                       a);
     return;
   }
-  hipLaunchKernelGGL((k_layer_down_combine<FMT, NT>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256), lds.down,
-                     s, a);
+  hipLaunchKernelGGL((k_layer_down_combine<FMT, NT, GP, IP>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256),
+                     lds.down, s, a);
+}
+
+// The Flint shape (hidden 2048, inter 768, the shared expert as wide as the
+// routed ones) runs kernels compiled for it; every other shape the same
+// kernels with its runtime shape.  Measured (NVFP4, 1/4/16/64 tokens):
+// 21.9/38.8/78.3/190 -> 20.4/34.6/68.1/148 us.  INT4 with several tokens
+// keeps the runtime shape: compiled for the Flint shape its gate/up spills
+// (78 registers at its 128-register bound) and its down needs 180
+// registers, 2.6x slower; one INT4 token gains (24.3 -> 21.4 us).
+template <int FMT, int NT>
+static void launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
+  if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && (FMT == kFmtNvfp4 || NT == 1))
+    launch_all<FMT, NT, 64, 24>(a, lds, s);
+  else
+    launch_all<FMT, NT, 0, 0>(a, lds, s);
 }
 
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
@@ -905,11 +953,11 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const bool nv = L->experts.gate.fmt == kFmtNvfp4;
   if (NT == 1)
-    nv ? launch_all<kFmtNvfp4, 1>(a, lds, s) : launch_all<kFmtInt4, 1>(a, lds, s);
+    nv ? launch_shape<kFmtNvfp4, 1>(a, lds, s) : launch_shape<kFmtInt4, 1>(a, lds, s);
   else if (NT == 2)
-    nv ? launch_all<kFmtNvfp4, 2>(a, lds, s) : launch_all<kFmtInt4, 2>(a, lds, s);
+    nv ? launch_shape<kFmtNvfp4, 2>(a, lds, s) : launch_shape<kFmtInt4, 2>(a, lds, s);
   else
-    nv ? launch_all<kFmtNvfp4, 4>(a, lds, s) : launch_all<kFmtInt4, 4>(a, lds, s);
+    nv ? launch_shape<kFmtNvfp4, 4>(a, lds, s) : launch_shape<kFmtInt4, 4>(a, lds, s);
   return hipGetLastError();
 }
 

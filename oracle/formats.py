@@ -17,6 +17,10 @@ a group-64 affine INT4 build.  The readings taken here:
   consecutive elements along the reduction axis) * e2m1 code.
 * INT4 group-64 affine weight = fp16 scale * (q - z), q and z in 0..15,
   one (scale, zero) per 64 consecutive elements along the reduction axis.
+* The other reading of "affine" (scale and bias, as MLX stores its affine
+  4-bit groups): weight = fp16 scale * q + fp16 bias, q in 0..15, one
+  (scale, bias) per 64 consecutive elements along the reduction axis.  The
+  zero-point form is the special case bias = -scale * z.
 * A matrix is stored row-major as [out, in]; element 2i of a row sits in
   the low nibble of byte i, element 2i+1 in the high nibble.
 
@@ -24,13 +28,15 @@ A matrix is a dict: ``fmt`` (1 = NVFP4, 2 = INT4 group 64), ``codes``
 uint8 [E, rows, cols/2], ``scales`` (NVFP4: uint8 e4m3 codes
 [E, rows, cols/16]; INT4: uint16 fp16 bit patterns [E, rows, cols/64]),
 ``zeros`` (INT4: uint8 [E, rows, cols/64]; else None), ``tensor_scale``
-(NVFP4: float32 [E]; else None).
+(NVFP4: float32 [E]; else None), ``biases`` (INT4 scale + bias: uint16 fp16
+bit patterns [E, rows, cols/64]; else absent or None).
 """
 
 import numpy as np
 
 FMT_NVFP4 = 1
 FMT_INT4_G64 = 2
+FMT_INT4_SB = 3
 NVFP4_BLOCK = 16
 INT4_GROUP = 64
 
@@ -90,6 +96,13 @@ def dequant_matrix(mat, expert):
         z = np.asarray(mat["zeros"][expert]).astype(np.float64)
         assert s.shape == (rows, cols // INT4_GROUP) and z.shape == s.shape
         return np.repeat(s, INT4_GROUP, axis=1) * (q - np.repeat(z, INT4_GROUP, axis=1))
+    if mat["fmt"] == FMT_INT4_SB:
+        # s*q has at most 15 significant bits and s*q + b spans at most 45 bits
+        # (fp16 magnitudes 2**-24 .. 2**20): exact in float64
+        s = fp16_bits_to_f64(mat["scales"][expert])          # [rows, cols/64]
+        b = fp16_bits_to_f64(mat["biases"][expert])
+        assert s.shape == (rows, cols // INT4_GROUP) and b.shape == s.shape
+        return np.repeat(s, INT4_GROUP, axis=1) * q + np.repeat(b, INT4_GROUP, axis=1)
     raise ValueError("unknown weight format %r" % (mat["fmt"],))
 
 
@@ -98,8 +111,9 @@ def dequant_matrix_f32(mat, expert):
 
     For NVFP4, block scale * code has at most 6 significant bits, so the
     float64 product with the fp32 tensor scale is exact and this is a single
-    rounding of the true value.  INT4 weights (at most 15 significant bits)
-    are exact in float32.
+    rounding of the true value.  INT4 zero-point weights (at most 15
+    significant bits) are exact in float32; scale + bias weights are exact in
+    float64, so this is again one rounding of the true value.
     """
     return dequant_matrix(mat, expert).astype(np.float32)
 

@@ -141,3 +141,60 @@ def test_dequant_f32_is_one_rounding_of_exact_product():
         b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float()[torch.from_numpy(scales[e].astype(np.int64))]
         ref = (b.repeat_interleave(16, dim=1) * q) * torch.tensor(ts[e])
         assert np.array_equal(got, ref.numpy())
+
+
+def test_dequant_int4_scale_bias_hand_values():
+    # 1 expert, 2 rows x 128 columns; every byte holds codes (c % 16, 15 - c % 16).
+    # Row 0: group 0 scale 0.5, bias -1.25; group 1 scale 2.0, bias 3.0.
+    # Row 1: group 0 scale -0.25, bias 0; group 1 scale 0 (bias only), bias -7.5.
+    codes = np.array([[[(i % 16) | ((15 - i % 16) << 4) for i in range(64)]] * 2], dtype=np.uint8)
+    h = lambda v: np.array(v, dtype=np.float16).view(np.uint16)
+    mat = {"fmt": 3, "codes": codes, "scales": h([[[0.5, 2.0], [-0.25, 0.0]]]),
+           "biases": h([[[-1.25, 3.0], [0.0, -7.5]]]), "zeros": None, "tensor_scale": None}
+    w = oracle.dequant_matrix(mat, 0)
+    for c in range(128):
+        i = c // 2
+        q = (i % 16) if c % 2 == 0 else 15 - (i % 16)
+        assert w[0, c] == (0.5 * q - 1.25 if c < 64 else 2.0 * q + 3.0), c
+        assert w[1, c] == (-0.25 * q if c < 64 else -7.5), c
+    # spot values: code 0 gives the bias, code 15 the top of the group's range
+    assert w[0, 0] == -1.25 and w[0, 1] == 6.25 and w[0, 64] == 3.0 and w[0, 65] == 33.0
+
+
+def test_dequant_int4_scale_bias_reduces_to_zero_point():
+    # With bias = -scale * z (exact: power-of-two scales) the scale+bias form equals the
+    # zero-point form element for element.
+    rng = np.random.default_rng(5)
+    E, rows, cols = 2, 8, 256
+    codes = rng.integers(0, 256, size=(E, rows, cols // 2), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(E, rows, cols // 64), dtype=np.uint8)
+    s = np.exp2(rng.integers(-12, 4, size=zeros.shape)).astype(np.float16)
+    s[0, 0, 0] = -s[0, 0, 0]
+    b = (-(s.astype(np.float64) * zeros)).astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), -(s.astype(np.float64) * zeros))   # the biases are exact
+    zp = {"fmt": 2, "codes": codes, "scales": s.view(np.uint16), "zeros": zeros, "tensor_scale": None}
+    sb = {"fmt": 3, "codes": codes, "scales": s.view(np.uint16), "biases": b.view(np.uint16), "zeros": None,
+          "tensor_scale": None}
+    for e in range(E):
+        assert np.array_equal(oracle.dequant_matrix(sb, e), oracle.dequant_matrix(zp, e))
+
+
+def test_dequant_int4_scale_bias_f32_is_one_rounding():
+    # fp16 scale * q + fp16 bias is exact in float64; the fp32 weight is its single rounding,
+    # which one float32 fused multiply-add also gives.  Scales and biases of very different
+    # magnitudes (up to 65504 against fp16 subnormals) make the sum inexact in float32.
+    rng = np.random.default_rng(6)
+    E, rows, cols = 1, 16, 512
+    codes = rng.integers(0, 256, size=(E, rows, cols // 2), dtype=np.uint8)
+    mag = np.exp2(rng.uniform(-24, 15.9, size=(E, rows, cols // 64)))
+    s = (mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float16)
+    b = (np.exp2(rng.uniform(-24, 15.9, size=mag.shape)) * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float16)
+    mat = {"fmt": 3, "codes": codes, "scales": s.view(np.uint16), "biases": b.view(np.uint16), "zeros": None,
+           "tensor_scale": None}
+    got = oracle.dequant_matrix_f32(mat, 0)
+    q = F.unpack_nibbles(codes[0]).astype(np.float64)
+    exact = np.repeat(s[0].astype(np.float64), 64, axis=1) * q + np.repeat(b[0].astype(np.float64), 64, axis=1)
+    # torch's float64 -> float32 conversion (one rounding, nearest even) of the exact value
+    ref = torch.from_numpy(exact).to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.any(ref.astype(np.float64) != exact)      # some sums really round

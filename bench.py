@@ -6,8 +6,9 @@ inter 768, NVFP4 W4A16 weights, bf16 activations).  One step = one
 moe_layer_decode call on one token: router GEMV, top-k + softmax, expert
 grouping, gate/up + SwiGLU, down projection, shared expert and combine.
 The same JSON line carries a ``sweep`` object with the rest of the metric:
-decode at 1/4/16/64 tokens in both weight formats, the 47-layer batch-8
-chained decode step, and the 4096-token Zipf(1.1) prefill in both formats,
+decode at 1/4/16/64 tokens in the three weight formats (NVFP4, INT4 with a
+zero point, INT4 with scale and bias), the 47-layer batch-8 chained decode
+step, and the 4096-token Zipf(1.1) prefill in NVFP4 and zero-point INT4,
 each with its roofline fraction and a short timing of the float64 CPU
 oracle on a bounded sample of the same workload.
 
@@ -19,7 +20,7 @@ one HIP graph; one warm replay, then one timed replay between HIP events on
 the launch stream.
 
 Single workloads (``--workload``): decode_b1, decode_T4, decode_T16,
-decode_T64 (with ``--fmt int4`` for the other format), chain_b8, prefill,
+decode_T64 (with ``--fmt int4`` or ``--fmt int4sb`` for the other formats), chain_b8, prefill,
 and hbm_copy: a plain 1 GiB device copy whose HBM counter readings calibrate
 the traffic figures.
 
@@ -63,7 +64,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="all")
-    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4"])
+    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4", "int4sb"])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the headline's CPU oracle leg")
     p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -439,7 +440,7 @@ def main():
     head = decode_entry(c, "nvfp4", 1, K, W, cpu)
     sweep = {}
     t_start = time.perf_counter()
-    for fmt_name in ("nvfp4", "int4"):
+    for fmt_name in ("nvfp4", "int4", "int4sb"):
         for T in (1, 4, 16, 64):
             if fmt_name == "nvfp4" and T == 1:
                 continue
@@ -450,6 +451,8 @@ def main():
             sweep["chain_b8_nvfp4"] = chain_entry(c, "nvfp4", Kc, Wc, scpu)
             print("[bench] chain done (%.0f s)" % (time.perf_counter() - t_start), file=sys.stderr, flush=True)
         c.drop(fmt_name)
+        if fmt_name == "int4sb":
+            continue       # the matrix-core grouped GEMM takes NVFP4 and zero-point INT4 only
         sweep["prefill_%s" % fmt_name] = prefill_entry(c, fmt_name, Kc, Wc, scpu)
         c.torch.cuda.empty_cache()
         print("[bench] prefill %s done (%.0f s)" % (fmt_name, time.perf_counter() - t_start), file=sys.stderr,

@@ -5,7 +5,8 @@ kernels.  The functions carry the C names (``moe_route``, ``moe_permute``,
 ``moe_grouped_w4a16_ffn``, ``moe_combine``, ``moe_layer_decode``, ...) and
 take torch tensors (their device pointers are passed through) plus packed
 weight dicts with keys ``fmt``, ``num_experts``, ``rows``, ``cols``,
-``codes``, ``scales``, ``zeros``, ``tensor_scale``.  Non-zero status codes
+``codes``, ``scales``, ``zeros``, ``tensor_scale`` and (scale + bias INT4)
+``biases``.  Non-zero status codes
 raise :class:`MoeError` with the library's message.
 
 If the shared library has not been built, importing this package raises
@@ -21,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, -1, -2, -3
-MOE_FMT_NVFP4, MOE_FMT_INT4_G64 = 1, 2
+MOE_FMT_NVFP4, MOE_FMT_INT4_G64, MOE_FMT_INT4_SB = 1, 2, 3
 MOE_MODE_AUTO, MOE_MODE_GEMV, MOE_MODE_MFMA = 0, 1, 2
 
 EXPORTED = [
@@ -41,7 +42,7 @@ class MoeError(RuntimeError):
 class W4Matrix(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int), ("num_experts", ctypes.c_int), ("rows", ctypes.c_int),
                 ("cols", ctypes.c_int), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("zeros", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+                ("zeros", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
 
 
 class FfnWeights(ctypes.Structure):
@@ -120,7 +121,8 @@ def moe_last_error():
 def w4_matrix(m):
     """A moe_w4_matrix from a packed-weight dict (torch tensors on the device)."""
     return W4Matrix(int(m["fmt"]), int(m["num_experts"]), int(m["rows"]), int(m["cols"]),
-                    _ptr(m["codes"]), _ptr(m["scales"]), _ptr(m.get("zeros")), _ptr(m.get("tensor_scale")))
+                    _ptr(m["codes"]), _ptr(m["scales"]), _ptr(m.get("zeros")), _ptr(m.get("tensor_scale")),
+                    _ptr(m.get("biases")))
 
 
 def ffn_weights(f):

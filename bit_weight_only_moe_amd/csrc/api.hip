@@ -47,7 +47,7 @@ constexpr int kMaxDim = 3840;
 
 // Validate one packed matrix stack against expected shape (0 = any).
 int check_matrix(const moe_w4_matrix& m, const char* name, int E, int rows, int cols) {
-  if (m.fmt != MOE_FMT_NVFP4 && m.fmt != MOE_FMT_INT4_G64)
+  if (m.fmt != MOE_FMT_NVFP4 && m.fmt != MOE_FMT_INT4_G64 && m.fmt != MOE_FMT_INT4_SB)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, m.fmt);
   if (m.num_experts < 1 || m.rows < 1 || m.cols < 64)
     return fail(MOE_ERR_INVALID_ARG, "%s: bad shape E=%d rows=%d cols=%d", name, m.num_experts, m.rows, m.cols);
@@ -62,6 +62,9 @@ int check_matrix(const moe_w4_matrix& m, const char* name, int E, int rows, int 
     return fail(MOE_ERR_INVALID_ARG, "%s: codes/scales not 16-byte aligned", name);
   if (m.fmt == MOE_FMT_NVFP4) {
     if (!m.tensor_scale) return fail(MOE_ERR_INVALID_ARG, "%s: NVFP4 needs tensor_scale", name);
+  } else if (m.fmt == MOE_FMT_INT4_SB) {
+    if (!m.biases || ((uintptr_t)m.biases & 1u))
+      return fail(MOE_ERR_INVALID_ARG, "%s: INT4 scale+bias needs 2-byte aligned biases", name);
   } else {
     if (!m.zeros) return fail(MOE_ERR_INVALID_ARG, "%s: INT4 needs zeros", name);
   }
@@ -200,7 +203,8 @@ int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream)
   const size_t e = (size_t)expert, R = (size_t)m->rows, C = (size_t)m->cols;
   const uint8_t* codes = m->codes + e * R * (C / 2);
   const uint8_t* scales = (const uint8_t*)m->scales + e * R * (m->fmt == MOE_FMT_NVFP4 ? C / 16 : (C / 64) * 2);
-  const uint8_t* zeros = m->zeros ? m->zeros + e * R * (C / 64) : nullptr;
+  const uint8_t* zeros = m->fmt == MOE_FMT_INT4_SB ? (const uint8_t*)m->biases + e * R * (C / 64) * 2
+                        : m->zeros ? m->zeros + e * R * (C / 64) : nullptr;
   const float* ts = m->tensor_scale ? m->tensor_scale + e : nullptr;
   return hip_status(moe::launch_dequant_expert(m->fmt, m->rows, m->cols, codes, scales, zeros, ts, out,
                                                as_stream(stream)),
@@ -276,9 +280,9 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
 // of 256 experts).
 constexpr int kAutoMfmaRowsPerExpert = 2;
 
-static bool use_mfma(int mode, int E, int H, int I, int total_rows) {
+static bool use_mfma(int mode, int fmt, int E, int H, int I, int total_rows) {
   if (mode == MOE_MODE_MFMA) return true;
-  if (mode == MOE_MODE_GEMV) return false;
+  if (mode == MOE_MODE_GEMV || fmt == MOE_FMT_INT4_SB) return false;
   return moe::mfma_shape_ok(H, I) && total_rows >= kAutoMfmaRowsPerExpert * E;
 }
 
@@ -304,7 +308,10 @@ int moe_grouped_w4a16_ffn(const moe_ffn_weights* w, int E, int H, int I, const u
   int rc = check_ffn(*w, "moe_grouped_w4a16_ffn.w", E, H, I);
   if (rc) return rc;
   if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_w4a16_ffn: x/out alignment");
-  const bool mfma = use_mfma(mode, E, H, I, total_rows);
+  const bool mfma = use_mfma(mode, w->gate.fmt, E, H, I, total_rows);
+  if (mfma && w->gate.fmt == MOE_FMT_INT4_SB)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: the matrix-core mode takes NVFP4 and INT4 zero-point "
+                "weights only (scale+bias runs the GEMV mode)");
   if (mfma && !moe::mfma_shape_ok(H, I))
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_w4a16_ffn: MFMA mode needs H %% 128 == 0 (H=%d)", H);
   const size_t need = mfma ? moe::mfma_ws_bytes(E, H, I, total_rows) : grouped_ws(E, I, total_rows, nullptr, nullptr, nullptr);
@@ -456,7 +463,7 @@ static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const 
     if (e == hipSuccess) e = hipMemcpyAsync(w_out, d.w, sizeof(float) * T * k, hipMemcpyDeviceToDevice, s);
   }
   if (e == hipSuccess) {
-    if (use_mfma(MOE_MODE_AUTO, E, H, L->I, T * k))
+    if (use_mfma(MOE_MODE_AUTO, L->experts.gate.fmt, E, H, L->I, T * k))
       e = moe::launch_grouped_mfma(&L->experts, E, d.offsets, d.sorted_pairs, k, x, H, L->I, T * k, d.o_routed,
                                    d.mfma_ws, s);
     else
@@ -464,7 +471,7 @@ static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const 
                                    L->I, d.h_routed, d.o_routed, T * k, s);
   }
   if (e == hipSuccess && L->shared) {
-    if (use_mfma(MOE_MODE_AUTO, 1, H, Is, T))
+    if (use_mfma(MOE_MODE_AUTO, L->shared->gate.fmt, 1, H, Is, T))
       e = moe::launch_grouped_mfma(L->shared, 1, nullptr, nullptr, 1, x, H, Is, T, d.o_shared, d.mfma_ws, s);
     else
       e = moe::launch_grouped_gemv(L->shared, nullptr, nullptr, nullptr, 1, 1, x, H, Is, d.h_shared, d.o_shared, T,

@@ -24,6 +24,7 @@ namespace moe {
 
 constexpr int kFmtNvfp4 = 1;
 constexpr int kFmtInt4 = 2;
+constexpr int kFmtInt4Sb = 3;  // INT4 with scale and bias per group of 64
 
 MOE_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 

@@ -90,7 +90,8 @@ MOE_DEV void stage_rows(uint16_t* __restrict__ dst, float* __restrict__ dsum, co
   }
 }
 
-// Raw bytes of one 32-weight piece: 16 bytes of codes, its scale bits and zero.
+// Raw bytes of one 32-weight piece: 16 bytes of codes, its scale bits and zero
+// (INT4 scale + bias: the bias bits).
 struct RawPiece {
   uint4 c;
   uint32_t s;
@@ -99,7 +100,7 @@ struct RawPiece {
 
 // Load piece p of a packed row.
 //   codes_row : K/2 bytes;  scales_row: NVFP4 K/16 e4m3 bytes, INT4 K/64 fp16
-//   zeros_row : INT4 K/64 bytes
+//   zeros_row : INT4 K/64 bytes; INT4 scale + bias: the biases, K/64 fp16
 template <int FMT>
 MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t* __restrict__ scales_row,
                             const uint8_t* __restrict__ zeros_row, int p) {
@@ -110,7 +111,7 @@ MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t
     r.z = 0;
   } else {
     r.s = ((const uint16_t*)scales_row)[p >> 1];
-    r.z = zeros_row[p >> 1];
+    r.z = FMT == kFmtInt4Sb ? (uint32_t)((const uint16_t*)zeros_row)[p >> 1] : (uint32_t)zeros_row[p >> 1];
   }
   return r;
 }
@@ -143,8 +144,13 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
     uint32_t rs = r.s, rz = r.z;
     asm volatile("" : "+v"(rs), "+v"(rz));
     b0 = f16_to_f32((unsigned short)rs);
-    b1 = 0.f;
-    zc = 128.0f + (float)rz;
+    if (FMT == kFmtInt4Sb) {
+      // sum (s q + b) x = s sum (128 + q) x + (b - 128 s) sum x
+      b1 = f16_to_f32((unsigned short)rz) - 128.0f * b0;
+    } else {
+      b1 = 0.f;
+      zc = 128.0f + (float)rz;
+    }
     q[0] = int4x2_to_bf16_off128<0>(c.x); q[1] = int4x2_to_bf16_off128<1>(c.x);
     q[2] = int4x2_to_bf16_off128<2>(c.x); q[3] = int4x2_to_bf16_off128<3>(c.x);
     q[4] = int4x2_to_bf16_off128<0>(c.y); q[5] = int4x2_to_bf16_off128<1>(c.y);
@@ -171,6 +177,8 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
       if (FMT == kFmtNvfp4) {
         acc[t] = fmaf(b0, d0, acc[t]);
         acc[t] = fmaf(b1, d1, acc[t]);
+      } else if (FMT == kFmtInt4Sb) {
+        acc[t] = fmaf(b0, d0 + d1, fmaf(b1, xsum[t * sstride + p], acc[t]));
       } else {
         acc[t] = fmaf(b0, fmaf(-zc, xsum[t * sstride + p], d0 + d1), acc[t]);
       }
@@ -182,7 +190,7 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
 struct MatDev {
   const uint8_t* codes;
   const uint8_t* scales;
-  const uint8_t* zeros;
+  const uint8_t* zeros;      // INT4 zeros; scale + bias: the biases
   const float* ts;
   int rows, cols;
 };
@@ -194,8 +202,11 @@ template <int FMT>
 MOE_DEV const uint8_t* row_scales(const MatDev& m, int e, int r) {
   return m.scales + ((size_t)e * m.rows + r) * (size_t)(FMT == kFmtNvfp4 ? m.cols / 16 : (m.cols / 64) * 2);
 }
+// INT4 zeros (u8) or, for scale + bias, the biases (fp16) of row r.
+template <int FMT>
 MOE_DEV const uint8_t* row_zeros(const MatDev& m, int e, int r) {
-  return m.zeros ? m.zeros + ((size_t)e * m.rows + r) * (size_t)(m.cols / 64) : nullptr;
+  return m.zeros ? m.zeros + ((size_t)e * m.rows + r) * (size_t)(FMT == kFmtInt4Sb ? (m.cols / 64) * 2 : m.cols / 64)
+                 : nullptr;
 }
 template <int FMT>
 MOE_DEV float tensor_scale(const MatDev& m, int e) {

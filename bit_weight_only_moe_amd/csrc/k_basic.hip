@@ -36,6 +36,13 @@ __global__ void __launch_bounds__(256) k_dequant_dev_ts(int fmt, int rows, int c
     v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (b * v[i]) * ts;
+  } else if (fmt == kFmtInt4Sb) {
+    // one fused multiply-add: the single rounding of s * q + b
+    const size_t g = (size_t)r * (cols / 64) + c0 / 64;
+    const float s = f16_to_f32(((const uint16_t*)scales)[g]);
+    const float b = f16_to_f32(((const uint16_t*)zeros)[g]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(s, (float)((word >> (4 * i)) & 15u), b);
   } else {
     const size_t g = (size_t)r * (cols / 64) + c0 / 64;
     const float s = f16_to_f32(((const uint16_t*)scales)[g]);

@@ -117,8 +117,8 @@ MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, 
     const int i = row0 + row_step * (c / ppl);
     if (c < npc && i < i1) {
       const int p = lir + (c % ppl) * lpr;
-      rg[q] = load_piece<FMT>(row_codes(G, e, i), row_scales<FMT>(G, e, i), row_zeros(G, e, i), p);
-      ru[q] = load_piece<FMT>(row_codes(U, e, i), row_scales<FMT>(U, e, i), row_zeros(U, e, i), p);
+      rg[q] = load_piece<FMT>(row_codes(G, e, i), row_scales<FMT>(G, e, i), row_zeros<FMT>(G, e, i), p);
+      ru[q] = load_piece<FMT>(row_codes(U, e, i), row_scales<FMT>(U, e, i), row_zeros<FMT>(U, e, i), p);
     }
   }
 }
@@ -228,7 +228,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
 #pragma unroll
     for (int q = 0; q < PC; ++q) {
       const int n = FIX ? row0 : row0 + 4 * rpw * (q / ppl);
-      if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
+      if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
                                                       lir + (FIX ? q : q % ppl) * lpr);
     }
   }
@@ -247,7 +247,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
           const int c = c0 + q;
           const int n = row0 + 4 * rpw * (c / ppl);
           if (c < npc && n < n1)
-            rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros(D, e, n),
+            rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
                                     lir + (c % ppl) * lpr);
         }
       }
@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
 // fits without spilling, 5 registers under its unbounded allocation, and
 // runs T=16/64 4-6% faster than at 3 waves)
 template <int FMT, int NT, int GP, int IP>
-__global__ void __launch_bounds__(256, FMT == kFmtInt4 && NT > 1 ? 4 : 1) k_layer_gateup(LayerArgs a) {
+__global__ void __launch_bounds__(256, FMT != kFmtNvfp4 && NT > 1 ? 4 : 1) k_layer_gateup(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_rec[kRec];
   const int unit = blockIdx.x / a.slices_r;
@@ -676,7 +676,7 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   {
     const uint8_t* rc = row_codes(D, e, nc);
     const uint8_t* rs = row_scales<FMT>(D, e, nc);
-    const uint8_t* rz = row_zeros(D, e, nc);
+    const uint8_t* rz = row_zeros<FMT>(D, e, nc);
 #pragma unroll
     for (int q = 0; q < kMaxPcD; ++q)
       if (q < ppl) rd[q] = load_piece<FMT>(rc, rs, rz, lir + q * lpr);
@@ -771,7 +771,7 @@ static MatDev mat_dev(const moe_w4_matrix& m) {
   MatDev d;
   d.codes = m.codes;
   d.scales = (const uint8_t*)m.scales;
-  d.zeros = m.zeros;
+  d.zeros = m.fmt == kFmtInt4Sb ? (const uint8_t*)m.biases : m.zeros;
   d.ts = m.tensor_scale;
   d.rows = m.rows;
   d.cols = m.cols;
@@ -844,6 +844,9 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   if (w->gate.fmt == kFmtNvfp4) {
     hipLaunchKernelGGL((k_grouped_gateup<kFmtNvfp4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
     hipLaunchKernelGGL((k_grouped_down<kFmtNvfp4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+  } else if (w->gate.fmt == kFmtInt4Sb) {
+    hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4Sb, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    hipLaunchKernelGGL((k_grouped_down<kFmtInt4Sb, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   } else {
     hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
     hipLaunchKernelGGL((k_grouped_down<kFmtInt4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
@@ -951,13 +954,16 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr);
   a.sync_slices = (a.H + kRDMin - 1) / kRDMin;
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
-  const bool nv = L->experts.gate.fmt == kFmtNvfp4;
-  if (NT == 1)
-    nv ? launch_shape<kFmtNvfp4, 1>(a, lds, s) : launch_shape<kFmtInt4, 1>(a, lds, s);
-  else if (NT == 2)
-    nv ? launch_shape<kFmtNvfp4, 2>(a, lds, s) : launch_shape<kFmtInt4, 2>(a, lds, s);
-  else
-    nv ? launch_shape<kFmtNvfp4, 4>(a, lds, s) : launch_shape<kFmtInt4, 4>(a, lds, s);
+  const int fmt = L->experts.gate.fmt;
+  auto by_fmt = [&](auto nt) {
+    constexpr int N = decltype(nt)::value;
+    if (fmt == kFmtNvfp4) launch_shape<kFmtNvfp4, N>(a, lds, s);
+    else if (fmt == kFmtInt4Sb) launch_shape<kFmtInt4Sb, N>(a, lds, s);
+    else launch_shape<kFmtInt4, N>(a, lds, s);
+  };
+  if (NT == 1) by_fmt(std::integral_constant<int, 1>{});
+  else if (NT == 2) by_fmt(std::integral_constant<int, 2>{});
+  else by_fmt(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 

@@ -894,6 +894,7 @@ static bool small_tiles_ok(int H, int I) { return I % 128 == 0 && H % 256 == 0; 
 hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* offsets, const int32_t* sorted_pairs,
                                int k, const uint16_t* x, int H, int I, int total_rows, float* out, void* ws,
                                hipStream_t s) {
+  if (w->gate.fmt != kFmtNvfp4 && w->gate.fmt != kFmtInt4) return hipErrorInvalidValue;  // NVFP4, INT4 only
   const size_t max_big = big_tiles_max(E, total_rows);
   int32_t* big = (int32_t*)ws;
   int32_t* small = big + 1 + 2 * max_big;

@@ -51,6 +51,15 @@
  *   INT4    (fmt 2) group-64 affine with zero point: scales = fp16
  *           [E, rows, cols/64], zeros = uint8 [E, rows, cols/64] in 0..15;
  *           w = scale * (code - zero).
+ *   INT4_SB (fmt 3) group-64 affine with scale and bias (the other reading
+ *           of "group-64 affine INT4" in the table under "What actually
+ *           shipped" of "Recursive Flint: 125 tok/s on an M4 Pro, measured
+ *           where it matters least"; MLX stores its affine groups so):
+ *           scales = fp16 [E, rows, cols/64], biases = fp16 [E, rows,
+ *           cols/64]; w = scale * code + bias (codes 0..15).  The zero-point
+ *           form is its special case bias = -scale * zero.  The matrix-core
+ *           grouped GEMM takes NVFP4 and INT4 only: scale+bias weights run the
+ *           GEMV kernels at every batch size.
  *   Gate and up are [I, H], down is [H, I].  H and I must be multiples of 64.
  */
 #ifndef MOE_W4A16_H
@@ -63,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum {
   MOE_OK = 0,
@@ -73,19 +82,20 @@ enum {
   MOE_ERR_HIP = -3          /* a HIP launch failed; see moe_last_error() */
 };
 
-enum { MOE_FMT_NVFP4 = 1, MOE_FMT_INT4_G64 = 2 };
+enum { MOE_FMT_NVFP4 = 1, MOE_FMT_INT4_G64 = 2, MOE_FMT_INT4_SB = 3 };
 enum { MOE_MODE_AUTO = 0, MOE_MODE_GEMV = 1, MOE_MODE_MFMA = 2 };
 
 /* One packed 4-bit matrix stack (host struct, device pointers). */
 typedef struct moe_w4_matrix {
-  int fmt;                   /* MOE_FMT_NVFP4 or MOE_FMT_INT4_G64 */
+  int fmt;                   /* MOE_FMT_NVFP4, MOE_FMT_INT4_G64 or MOE_FMT_INT4_SB */
   int num_experts;           /* E of this stack */
   int rows, cols;            /* out, in (cols = reduction axis); cols <= 3840 (the GEMV
                                 kernels stage 8 tokens' rows of cols in 64 KB of LDS) */
   const uint8_t* codes;      /* [E, rows, cols/2] */
-  const void* scales;        /* NVFP4: uint8 e4m3 [E, rows, cols/16]; INT4: fp16 [E, rows, cols/64] */
-  const uint8_t* zeros;      /* INT4: uint8 [E, rows, cols/64]; NVFP4: NULL */
-  const float* tensor_scale; /* NVFP4: fp32 [E]; INT4: NULL */
+  const void* scales;        /* NVFP4: uint8 e4m3 [E, rows, cols/16]; INT4, INT4_SB: fp16 [E, rows, cols/64] */
+  const uint8_t* zeros;      /* INT4: uint8 [E, rows, cols/64]; else NULL */
+  const float* tensor_scale; /* NVFP4: fp32 [E]; else NULL */
+  const void* biases;        /* INT4_SB: fp16 [E, rows, cols/64]; else NULL */
 } moe_w4_matrix;
 
 /* A SwiGLU expert stack: gate [I, H], up [I, H], down [H, I]; same fmt. */

@@ -17,6 +17,9 @@ Value recipes (no trained weights exist here; these stand in for them):
                   over the 16 e4m3 codes 0x30..0x3F (values in [0.5, 2));
                   tensor scale ~ U(0.004, 0.008) per (expert, matrix)
   INT4 group 64   codes uniform; fp16 scale ~ U(0.005, 0.02); zero U{0..15}
+  INT4 scale+bias codes uniform; fp16 scale ~ U(0.005, 0.02); fp16 bias =
+                  -scale * U(6.5, 8.5) (groups roughly centred on zero, as a
+                  min/max affine quantiser gives them)
   full-range scales (scale_range="full", for parity cases that cover the
                   whole of both scale formats):
                   NVFP4 block scales uniform over all 254 non-NaN e4m3 codes
@@ -25,7 +28,9 @@ Value recipes (no trained weights exist here; these stand in for them):
                   times that of the codes 0x30..0x3F), so the weight RMS
                   stays near 1/sqrt(H); INT4 fp16 scales with a random sign,
                   10% of them fp16 subnormals U(2**-24, 2**-14), 5% zeros
-                  (signed), the rest U(0.005, 0.02)
+                  (signed), the rest U(0.005, 0.02); scale+bias INT4 draws its
+                  scales so and its biases as -scale * U(6.5, 8.5) with 10% of
+                  them fp16 subnormals of either sign
   routing logits  "uniform": fp32 ~ U(0, 1) i.i.d.;
                   "zipf": log p(rank(e)) + Gumbel(0, 1), p(r) ~ r**-s over
                   a seeded permutation of the experts (Gumbel-top-k draws k
@@ -37,7 +42,8 @@ import torch
 
 FMT_NVFP4 = 1
 FMT_INT4_G64 = 2
-FMT_NAMES = {"nvfp4": FMT_NVFP4, "int4": FMT_INT4_G64}
+FMT_INT4_SB = 3
+FMT_NAMES = {"nvfp4": FMT_NVFP4, "int4": FMT_INT4_G64, "int4sb": FMT_INT4_SB}
 
 
 def seed_of(*keys):
@@ -86,6 +92,26 @@ def make_matrix(fmt, num_experts, rows, cols, seed, device="cpu", scale_range="n
             s = s * sign.to(torch.float32)
         return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols,
                 "codes": codes, "scales": s.to(torch.float16), "zeros": zeros, "tensor_scale": None}
+    if fmt == FMT_INT4_SB:
+        shape = (E, rows, cols // 64)
+        s = (torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 0.015 + 0.005)
+        if scale_range == "full":
+            kind = torch.rand(shape, dtype=torch.float32, device=device, generator=g)
+            sub = torch.exp2(torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 10.0 - 24.0)
+            s = torch.where(kind < 0.10, sub, s)
+            s = torch.where((kind >= 0.10) & (kind < 0.15), torch.zeros_like(s), s)
+            sign = torch.randint(0, 2, shape, dtype=torch.int32, device=device, generator=g) * 2 - 1
+            s = s * sign.to(torch.float32)
+        s = s.to(torch.float16).to(torch.float32)
+        b = -s * (torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 2.0 + 6.5)
+        if scale_range == "full":
+            kind = torch.rand(shape, dtype=torch.float32, device=device, generator=g)
+            sub = torch.exp2(torch.rand(shape, dtype=torch.float32, device=device, generator=g) * 10.0 - 24.0)
+            sign = torch.randint(0, 2, shape, dtype=torch.int32, device=device, generator=g) * 2 - 1
+            b = torch.where(kind < 0.10, sub * sign.to(torch.float32), b)
+        return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols,
+                "codes": codes, "scales": s.to(torch.float16), "zeros": None, "tensor_scale": None,
+                "biases": b.to(torch.float16)}
     raise ValueError("unknown format %r" % (fmt,))
 
 
@@ -154,8 +180,8 @@ def _np_expert_slice(t, experts):
 def matrix_to_numpy(mat, experts=None):
     """Host copy of a packed matrix; with ``experts``, only those (a dict by id)."""
     out = {"fmt": mat["fmt"], "num_experts": mat["num_experts"], "rows": mat["rows"], "cols": mat["cols"]}
-    for key in ("codes", "scales", "zeros", "tensor_scale"):
-        out[key] = _np_expert_slice(mat[key], experts)
+    for key in ("codes", "scales", "zeros", "tensor_scale", "biases"):
+        out[key] = _np_expert_slice(mat.get(key), experts)
     return out
 
 
@@ -175,6 +201,8 @@ def matrix_bytes(fmt, rows, cols):
     n = rows * cols
     if fmt == FMT_NVFP4:
         return n // 2 + n // 16 + 4
+    if fmt == FMT_INT4_SB:
+        return n // 2 + 2 * (n // 64) + 2 * (n // 64)
     return n // 2 + 2 * (n // 64) + n // 64
 
 

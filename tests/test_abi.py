@@ -36,7 +36,8 @@ FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced (valida
 
 def fake_matrix(fmt=1, E=4, rows=128, cols=256, codes=FAKE, scales=FAKE):
     return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols, "codes": codes, "scales": scales,
-            "zeros": FAKE if fmt == 2 else None, "tensor_scale": FAKE if fmt == 1 else None}
+            "zeros": FAKE if fmt == 2 else None, "tensor_scale": FAKE if fmt == 1 else None,
+            "biases": FAKE if fmt == 3 else None}
 
 
 def fake_ffn(fmt=1, E=4, H=256, I=128):
@@ -101,7 +102,7 @@ def test_grouped_ffn_validation():
     expect(uns, moe.moe_grouped_w4a16_ffn, f, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, mode=7, ws=FAKE,
            ws_bytes=need)
     bad = fake_ffn()
-    bad["up"]["fmt"] = 3
+    bad["up"]["fmt"] = 4
     expect(uns, moe.moe_grouped_w4a16_ffn, bad, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, ws=FAKE, ws_bytes=need)
     mixed = fake_ffn()
     mixed["down"] = fake_matrix(2, 4, 256, 128)
@@ -114,6 +115,15 @@ def test_grouped_ffn_validation():
     unaligned["down"]["codes"] = FAKE + 8
     expect(inv, moe.moe_grouped_w4a16_ffn, unaligned, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, ws=FAKE,
            ws_bytes=need)
+    # scale + bias INT4: needs its biases; the matrix-core mode does not take it
+    sb = fake_ffn(fmt=3)
+    need_sb = moe.moe_grouped_ffn_workspace_size(4, 256, 128, 24, moe.MOE_MODE_MFMA)
+    msg = expect(uns, moe.moe_grouped_w4a16_ffn, sb, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, mode=moe.MOE_MODE_MFMA,
+                 ws=FAKE, ws_bytes=need_sb)
+    assert "scale+bias" in msg
+    nob = fake_ffn(fmt=3)
+    nob["down"]["biases"] = None
+    expect(inv, moe.moe_grouped_w4a16_ffn, nob, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, ws=FAKE, ws_bytes=need)
     # at most 3840 columns per matrix (the header's limit); 3840 itself passes validation
     need_w = moe.moe_grouped_ffn_workspace_size(4, 3904, 128, 24)
     msg = expect(uns, moe.moe_grouped_w4a16_ffn, fake_ffn(H=3904), 4, 3904, 128, FAKE, FAKE, 6, FAKE, 24, FAKE,

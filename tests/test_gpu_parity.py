@@ -55,16 +55,38 @@ def exhaustive_int4(device):
             "scales": t(scales).view(torch.float16), "zeros": t(zeros), "tensor_scale": None}
 
 
-@pytest.mark.parametrize("which", ["nvfp4_exhaustive", "int4_exhaustive", "nvfp4_flint", "int4_flint"])
+def exhaustive_int4_sb(device):
+    # every code against 16 scales x 16 biases (fp16 extremes, subnormals, signs, -0): rows r
+    # takes bias r, group g scale g, so all 16 x 16 x 16 (code, scale, bias) combinations occur
+    rows, cols = 16, 1024
+    i = np.arange(cols // 2)
+    row_bytes = ((2 * i) % 16) | (((2 * i + 1) % 16) << 4)
+    codes = np.broadcast_to(row_bytes.astype(np.uint8), (1, rows, cols // 2)).copy()
+    svals = np.array([1.0, -0.5, 0.0071234, 65504.0, 6.103515625e-05, 5.960464477539063e-08, 0.0123, -3.75,
+                      0.005, 0.02, 1.5, 2.0 ** -10, 7.0, -0.0, 100.0, 0.333], dtype=np.float16)
+    bvals = np.array([0.0, -1.25, 3.0, -65504.0, 5.960464477539063e-08, -6.0e-05, 0.1, -0.0, 1e-3, -7.5,
+                      2048.0, 0.333, -0.0071234, 12.0, -1.0, 6.103515625e-05], dtype=np.float16)
+    scales = np.broadcast_to(svals.view(np.uint16)[None, None, :], (1, rows, cols // 64)).copy()
+    biases = np.broadcast_to(bvals.view(np.uint16)[None, :, None], (1, rows, cols // 64)).copy()
+    t = lambda a: torch.from_numpy(a).to(device)
+    return {"fmt": 3, "num_experts": 1, "rows": rows, "cols": cols, "codes": t(codes),
+            "scales": t(scales).view(torch.float16), "zeros": None, "tensor_scale": None,
+            "biases": t(biases).view(torch.float16)}
+
+
+@pytest.mark.parametrize("which", ["nvfp4_exhaustive", "int4_exhaustive", "int4sb_exhaustive", "nvfp4_flint",
+                                   "int4_flint", "int4sb_flint"])
 def test_dequant_bit_exact(which):
     print("dequant", which, flush=True)
     if which == "nvfp4_exhaustive":
         mat = exhaustive_nvfp4(DEV)
     elif which == "int4_exhaustive":
         mat = exhaustive_int4(DEV)
+    elif which == "int4sb_exhaustive":
+        mat = exhaustive_int4_sb(DEV)
     else:
-        fmt = 1 if which.startswith("nvfp4") else 2
-        mat = synth.make_matrix(fmt, 4, 768, 2048, seed=21, device=DEV)
+        fmt = {"nvfp4": 1, "int4": 2, "int4sb": 3}[which.split("_")[0]]
+        mat = synth.make_matrix(fmt, 4, 768, 2048, seed=21, device=DEV, scale_range="full")
     host = synth.matrix_to_numpy(mat)
     for e in range(mat["num_experts"]):
         out = torch.empty((mat["rows"], mat["cols"]), dtype=torch.float32, device=DEV)
@@ -232,7 +254,9 @@ FFN_CASES = [
     (2, 3840, 256, 16, 4, 3, 54),     # the largest K: pieces streamed in chunks
 ]
 # every non-NaN e4m3 block scale (both signs, subnormals, 448) / signed, subnormal and zero fp16 scales
-FFN_CASES_FULL = [(1, 2048, 768, 256, 6, 5, 55), (2, 2048, 768, 256, 6, 5, 56), (1, 192, 320, 8, 3, 9, 57)]
+FFN_CASES_FULL = [(1, 2048, 768, 256, 6, 5, 55), (2, 2048, 768, 256, 6, 5, 56), (1, 192, 320, 8, 3, 9, 57),
+                  (3, 2048, 768, 256, 6, 5, 58), (3, 192, 320, 8, 3, 9, 59)]
+FFN_CASES = FFN_CASES + [(3, 2048, 768, 256, 6, 5, 60), (3, 256, 128, 32, 6, 4, 61)]
 
 
 @pytest.mark.parametrize("fmt,H,I,E,k,T,seed,scales", [c + ("narrow",) for c in FFN_CASES] +
@@ -373,6 +397,12 @@ LAYER_CASES = [
     # the largest supported hidden size (3840 columns)
     ("big_H3840_T1", 1, 3840, 512, 64, 4, 1, 22, True),
     ("big_int4_H3840_T8", 2, 3840, 512, 64, 4, 8, 23, False),
+    # INT4 with scale and bias per group of 64
+    ("tiny_int4sb_T4", 3, 256, 128, 32, 6, 4, 24, True),
+    ("flint_int4sb_T1", 3, 2048, 768, 256, 6, 1, 25, True),
+    ("flint_int4sb_T4", 3, 2048, 768, 256, 6, 4, 26, False),
+    ("flint_int4sb_T16", 3, 2048, 768, 256, 6, 16, 27, True),
+    ("ragged_int4sb_H192_I320_T1", 3, 192, 320, 8, 6, 1, 28, False),
 ]
 
 
@@ -406,7 +436,7 @@ def test_layer_decode_T64_sampled(fmt):
     check_layer(layer, x, x, y, ids, w, tokens=[0, 17, 31, 40, 63], ws=ws)
 
 
-@pytest.mark.parametrize("fmt,T", [(1, 1), (2, 1), (2, 4), (1, 16), (2, 16)])
+@pytest.mark.parametrize("fmt,T", [(1, 1), (2, 1), (2, 4), (1, 16), (2, 16), (3, 1), (3, 16)])
 def test_layer_decode_full_scale_range(fmt, T):
     """Flint-shaped layer whose block scales cover the whole format: every
     non-NaN e4m3 code (both signs, subnormals, up to 448) for NVFP4; signed,
@@ -742,7 +772,7 @@ def test_prefill_4096_zipf_sampled():
     assert err <= TOL_LAYER
 
 
-@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100)])
+@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100), (3, 100)])
 def test_layer_decode_large_batch_uses_grouped_gemm(fmt, T):
     """Above 64 tokens the layer is composed from the separate calls; 70 tokens
     (420 pairs, under two per expert) take the GEMV grouped FFN, 100 and 200

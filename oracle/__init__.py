@@ -49,4 +49,5 @@ from .moe import (  # noqa: F401
     moe_layer,
     rms_norm,
     chain_layer,
+    dense_gemv,
 )

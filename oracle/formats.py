@@ -82,8 +82,19 @@ def unpack_nibbles(codes):
     return out
 
 
-def dequant_matrix(mat, expert):
-    """Exact float64 weights [rows, cols] of one expert of a packed matrix."""
+def _rows(a, rows):
+    a = np.asarray(a)
+    return a if rows is None else a[np.asarray(rows)]
+
+
+def dequant_matrix(mat, expert, rows=None):
+    """Exact float64 weights [rows, cols] of one expert of a packed matrix
+    (only the listed rows when ``rows`` is given)."""
+    sub = dict(mat)
+    for key in ("codes", "scales", "zeros", "biases"):
+        if mat.get(key) is not None:
+            sub[key] = {expert: _rows(mat[key][expert], rows)}
+    mat = sub
     q = unpack_nibbles(mat["codes"][expert])
     rows, cols = q.shape
     if mat["fmt"] == FMT_NVFP4:

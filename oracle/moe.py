@@ -190,3 +190,12 @@ def chain_layer(layer, r_bits, eps, logits=None):
     Returns (x_bits, the moe_layer result dict)."""
     x_bits = rms_norm(r_bits, eps)
     return x_bits, moe_layer(layer, x_bits, residual_bits=r_bits, logits=logits)
+
+
+def dense_gemv(mat, expert, x_bits, rows=None):
+    """out[t, n] = sum_c W[n, c] x[t, c] for one packed 4-bit matrix (the
+    4-bit output head of "Recursive Flint: 40B Local Coding Model,
+    Benchmarks", section "How Recursive built Flint", is such a matrix over
+    the 150,144-token vocabulary).  ``rows`` restricts it to those output rows."""
+    x = bf16_bits_to_f64(x_bits)
+    return x @ dequant_matrix(mat, expert, rows).T

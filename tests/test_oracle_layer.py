@@ -164,3 +164,22 @@ def test_zero_down_weights_pass_the_residual_through():
     out = oracle.moe_layer(L, xb, residual_bits=xb)
     assert np.array_equal(out["y"], oracle.bf16_bits_to_f64(xb))
     assert np.array_equal(f64_to_bf16_bits(out["y_bf16"]), xb)
+
+
+def test_dense_gemv_one_hot_columns_and_row_subsets():
+    """The dense product against one-hot tokens returns the dequantised columns
+    exactly, a row subset equals those rows of the full product, and the
+    subset dequantisation equals the full one's rows (all three formats)."""
+    rng = np.random.default_rng(11)
+    for fmt in (1, 2, 3):
+        m = synth.matrix_to_numpy(synth.make_matrix(fmt, 2, 40, 128, seed=fmt, device="cpu"))
+        w = dequant_matrix(m, 1)
+        cols = np.array([0, 5, 63, 64, 127])
+        x = np.zeros((len(cols), 128))
+        x[np.arange(len(cols)), cols] = 1.0
+        out = oracle.dense_gemv(m, 1, f64_to_bf16_bits(x))
+        assert np.array_equal(out, w[:, cols].T)
+        rows = np.array([39, 0, 17, 17])
+        assert np.array_equal(dequant_matrix(m, 1, rows), w[rows])
+        xt = f64_to_bf16_bits(rne_bf16(rng.standard_normal((3, 128))))
+        assert np.array_equal(oracle.dense_gemv(m, 1, xt, rows), oracle.dense_gemv(m, 1, xt)[:, rows])

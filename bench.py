@@ -19,8 +19,12 @@ flushed (a 1 GiB copy) before each timed replay.  K steps are captured in
 one HIP graph; one warm replay, then one timed replay between HIP events on
 the launch stream.
 
+The sweep also carries the dense 4-bit output-head GEMV (150,144 x 2048,
+1 and 8 tokens).
+
 Single workloads (``--workload``): decode_b1, decode_T4, decode_T16,
 decode_T64 (with ``--fmt int4`` or ``--fmt int4sb`` for the other formats), chain_b8, prefill,
+dense_head (``--tokens T``),
 and hbm_copy: a plain 1 GiB device copy whose HBM counter readings calibrate
 the traffic figures.
 
@@ -68,6 +72,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the headline's CPU oracle leg")
     p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--tokens", type=int, default=1, help="tokens of the dense_head workload")
     return p.parse_args()
 
 
@@ -366,6 +371,52 @@ def prefill_entry(c, fmt_name, K, W, cpu_seconds):
     return entry
 
 
+def dense_entry(c, fmt_name, T, K, W, cpu_seconds, rows=150144):
+    """The 4-bit output head: out[T, 150144] = W x over hidden 2048, one matrix
+    per step, rotating over copies of more than 512 MB in all."""
+    t, moe, synth = c.torch, c.moe, c.synth
+    fmt = synth.FMT_NAMES[fmt_name]
+    mb = synth.matrix_bytes(fmt, rows, H)
+    R = max(2, math.ceil(ROTATE_BYTES / mb))
+    mats = [synth.make_matrix(fmt, 1, rows, H, synth.seed_of(6, r), c.dev) for r in range(R)]
+    NX = max(K, W, 1)
+    xs = [synth.make_tokens(T, H, synth.seed_of(7, T, i), c.dev) for i in range(NX)]
+    out = t.empty((T, rows), dtype=t.float32, device=c.dev)
+
+    def step(i, s):
+        moe.moe_dense_w4a16_gemv(mats[i % R], 0, xs[i % NX], T, out, stream=s)
+
+    ms = c.timed(step, K, W)
+    ms_step = ms / K
+    gbs = mb * ((T + 7) // 8) / (ms_step * 1e-3) / 1e9
+    entry = {"workload": "dense_w4a16_gemv output head %d x 2048 T=%d %s" % (rows, T, fmt_name),
+             "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
+             "weight_copies": R, "matrix_bytes": mb,
+             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                          "kernel": "k_dense_gemv (one call), events on the launch stream",
+                          "bytes": "the packed matrix once per batch of up to 8 tokens"},
+             "cpu_baseline": None}
+    if cpu_seconds > 0:
+        import oracle
+        host = synth.matrix_to_numpy(mats[0])
+        xb = synth.bits16(xs[0])
+        n = 4096
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.dense_gemv(host, 0, xb, rows=np.arange(done * n % rows, done * n % rows + n) % rows)
+            done += 1
+            if time.perf_counter() - t0 >= cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        full_s = el / (done * n) * rows
+        entry["cpu_baseline"] = cpu_entry(T / full_s, "tokens/s",
+                                          "%d oracle runs over 4096 of the 150,144 rows (%s, T=%d), %.1f s incl. "
+                                          "dequantisation, scaled to the full head" % (done, fmt_name, T, el))
+    return entry
+
+
 def copy_line(c, args):
     """A plain device copy of 1 GiB (torch's copy kernel): 1 GiB read + 1 GiB written per step."""
     t = c.torch
@@ -423,6 +474,10 @@ def main():
         e = decode_entry(c, args.fmt, decode_T[wl], K, W, cpu)
         print(json.dumps(line_from(e, args.fmt, "tokens_per_s", "tokens/s", K, W)))
         return
+    if wl == "dense_head":
+        e = dense_entry(c, args.fmt, args.tokens, K, W, cpu)
+        print(json.dumps(line_from(e, args.fmt, "tokens_per_s", "tokens/s", K, W)))
+        return
     if wl == "chain_b8":
         e = chain_entry(c, args.fmt, Kc, Wc, cpu)
         print(json.dumps(line_from(e, args.fmt, "tokens_per_s", "tokens/s", Kc, Wc)))
@@ -456,6 +511,10 @@ def main():
         sweep["prefill_%s" % fmt_name] = prefill_entry(c, fmt_name, Kc, Wc, scpu)
         c.torch.cuda.empty_cache()
         print("[bench] prefill %s done (%.0f s)" % (fmt_name, time.perf_counter() - t_start), file=sys.stderr,
+              flush=True)
+    for T in (1, 8):
+        sweep["dense_head_T%d_nvfp4" % T] = dense_entry(c, "nvfp4", T, K, W, scpu)
+        print("[bench] dense head T=%d done (%.0f s)" % (T, time.perf_counter() - t_start), file=sys.stderr,
               flush=True)
     out = line_from(head, "nvfp4", "tokens_per_s", "tokens/s", K, W)
     out["sweep"] = sweep

@@ -29,7 +29,7 @@ EXPORTED = [
     "moe_abi_version", "moe_last_error", "moe_dequant_w4", "moe_route", "moe_topk_softmax",
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_ffn_workspace_size",
     "moe_grouped_w4a16_ffn", "moe_combine", "moe_layer_decode_workspace_size", "moe_layer_decode",
-    "moe_rms_norm", "moe_layer_decode_noalloc_max_bytes", "moe_layer_decode_noalloc",
+    "moe_rms_norm", "moe_layer_decode_noalloc_max_bytes", "moe_layer_decode_noalloc", "moe_dense_w4a16_gemv",
 ]
 
 
@@ -76,6 +76,7 @@ def _load():
         "moe_layer_decode": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, P, Z, S]),
         "moe_rms_norm": (I, [P, I, I, ctypes.c_float, P, S]),
         "moe_layer_decode_noalloc_max_bytes": (Z, []),
+        "moe_dense_w4a16_gemv": (I, [ctypes.POINTER(W4Matrix), I, P, I, P, S]),
         "moe_layer_decode_noalloc": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, S]),
     }
     for name, (res, args) in sig.items():
@@ -204,3 +205,8 @@ def moe_layer_decode_noalloc(layer, x, residual, T, y, ids_out=None, w_out=None,
     L = layer if isinstance(layer, Layer) else Layer(layer)
     return _check(_lib.moe_layer_decode_noalloc(ctypes.byref(L.c), _ptr(x), _ptr(residual), T, _ptr(y),
                                                 _ptr(ids_out), _ptr(w_out), _stream(stream)))
+
+
+def moe_dense_w4a16_gemv(mat, expert, x, T, out, stream=None):
+    m = w4_matrix(mat)
+    return _check(_lib.moe_dense_w4a16_gemv(ctypes.byref(m), int(expert), _ptr(x), T, _ptr(out), _stream(stream)))

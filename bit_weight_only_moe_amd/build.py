@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_w4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "k_basic.hip", "k_layer.hip", "k_mfma.hip"]
+SOURCES = ["api.hip", "k_basic.hip", "k_layer.hip", "k_mfma.hip", "k_dense.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

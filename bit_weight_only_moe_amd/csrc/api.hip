@@ -45,15 +45,17 @@ constexpr int kDecodeMaxT = 64;
 // Tokens are staged in LDS 8 at a time (8 * K * 2.125 bytes <= 64 KB).
 constexpr int kMaxDim = 3840;
 
-// Validate one packed matrix stack against expected shape (0 = any).
-int check_matrix(const moe_w4_matrix& m, const char* name, int E, int rows, int cols) {
+// Validate one packed matrix stack against expected shape (0 = any).  max_rows:
+// 65536 for expert matrices; the dense GEMV takes up to kDenseMaxRows.
+constexpr int kDenseMaxRows = 1 << 24;
+int check_matrix(const moe_w4_matrix& m, const char* name, int E, int rows, int cols, int max_rows = 65536) {
   if (m.fmt != MOE_FMT_NVFP4 && m.fmt != MOE_FMT_INT4_G64 && m.fmt != MOE_FMT_INT4_SB)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, m.fmt);
   if (m.num_experts < 1 || m.rows < 1 || m.cols < 64)
     return fail(MOE_ERR_INVALID_ARG, "%s: bad shape E=%d rows=%d cols=%d", name, m.num_experts, m.rows, m.cols);
   if (m.cols % 64) return fail(MOE_ERR_INVALID_ARG, "%s: cols=%d is not a multiple of 64", name, m.cols);
-  if (m.cols > kMaxDim || m.rows > 65536)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: cols=%d > %d or rows=%d > 65536", name, m.cols, kMaxDim, m.rows);
+  if (m.cols > kMaxDim || m.rows > max_rows)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: cols=%d > %d or rows=%d > %d", name, m.cols, kMaxDim, m.rows, max_rows);
   if ((E && m.num_experts != E) || (rows && m.rows != rows) || (cols && m.cols != cols))
     return fail(MOE_ERR_INVALID_ARG, "%s: shape [%d, %d, %d] does not match expected [%d, %d, %d]", name,
                 m.num_experts, m.rows, m.cols, E, rows, cols);
@@ -209,6 +211,19 @@ int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream)
   return hip_status(moe::launch_dequant_expert(m->fmt, m->rows, m->cols, codes, scales, zeros, ts, out,
                                                as_stream(stream)),
                     "moe_dequant_w4");
+}
+
+int moe_dense_w4a16_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out, void* stream) {
+  if (!m || !x || !out) return fail(MOE_ERR_INVALID_ARG, "moe_dense_w4a16_gemv: null argument");
+  int rc = check_matrix(*m, "moe_dense_w4a16_gemv.m", 0, 0, 0, kDenseMaxRows);
+  if (rc) return rc;
+  if (expert < 0 || expert >= m->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dense_w4a16_gemv: expert %d out of [0, %d)", expert, m->num_experts);
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_dense_w4a16_gemv: T=%d < 0", T);
+  if (!aligned16(x) || !aligned16(out))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dense_w4a16_gemv: x / out not 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_dense_gemv(m, expert, x, T, out, as_stream(stream)), "moe_dense_w4a16_gemv");
 }
 
 static int check_route_dims(const char* who, int T, int E, int k) {

@@ -11,6 +11,10 @@
 
 namespace moe {
 
+// Dense GEMV out[T, rows] = W_expert x (tokens in batches of dense_max_tokens()).
+int dense_max_tokens();
+hipError_t launch_dense_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
+                             hipStream_t s);
 hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* codes, const void* scales,
                                  const uint8_t* zeros, const float* ts_dev, float* out, hipStream_t s);
 // Router logits on the matrix cores (fp32 weights split exactly into three

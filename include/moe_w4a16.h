@@ -127,6 +127,20 @@ const char* moe_last_error(void);
  * (A test export: it states the format definition above as code.) */
 int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream);
 
+/* Dense 4-bit GEMV: out[t, n] = sum_c W[n, c] * x[t, c] for matrix `expert`
+ * of `m` (rows n < m->rows, up to 2^24; cols as for every matrix, a multiple
+ * of 64 up to 3840), x bf16 [T, cols], out fp32 [T, rows] (device,
+ * caller-owned, 16-byte aligned); weights exactly dequantised, fp32
+ * accumulation, the NVFP4 tensor scale applied last.  Tokens are taken in
+ * batches of 8, each batch streaming the matrix once.  Source: the 4-bit
+ * output head of "Recursive Flint: 40B Local Coding Model, Benchmarks"
+ * (section "How Recursive built Flint") over its 150,144-token vocabulary
+ * ("What is Recursive Flint?"); the same call serves any dense projection.
+ * Errors: MOE_ERR_INVALID_ARG for null or misaligned pointers, a bad expert
+ * or T < 0; MOE_ERR_UNSUPPORTED for more than 2^24 rows or 3840 columns. */
+int moe_dense_w4a16_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
+                         void* stream);
+
 /* Router: logits[t, e] = sum_h x[t, h] * w_router[e, h] (fp32 accumulation)
  * for x bf16 [T, H] and w_router fp32 [E, H] (both 16-byte aligned), then
  * top-k and softmax weights as in moe_topk_softmax: topk_ids int32 [T, k] in

@@ -256,7 +256,9 @@ FFN_CASES = [
 # every non-NaN e4m3 block scale (both signs, subnormals, 448) / signed, subnormal and zero fp16 scales
 FFN_CASES_FULL = [(1, 2048, 768, 256, 6, 5, 55), (2, 2048, 768, 256, 6, 5, 56), (1, 192, 320, 8, 3, 9, 57),
                   (3, 2048, 768, 256, 6, 5, 58), (3, 192, 320, 8, 3, 9, 59)]
-FFN_CASES = FFN_CASES + [(3, 2048, 768, 256, 6, 5, 60), (3, 256, 128, 32, 6, 4, 61)]
+FFN_CASES = FFN_CASES + [(3, 2048, 768, 256, 6, 5, 60), (3, 256, 128, 32, 6, 4, 61),
+                         # a dense FFN layer as the one-expert call (inter 3840 assumed; the pages give none)
+                         (1, 2048, 3840, 1, 1, 4, 62), (2, 2048, 3840, 1, 1, 8, 63)]
 
 
 @pytest.mark.parametrize("fmt,H,I,E,k,T,seed,scales", [c + ("narrow",) for c in FFN_CASES] +
@@ -289,6 +291,46 @@ def test_grouped_ffn_gemv(fmt, H, I, E, k, T, seed, scales):
     ref_s = oracle.grouped_ffn(host["shared"], xb, np.array([0, T]))
     assert normwise_err(out.cpu().numpy(), ref) <= TOL_EXPERT
     assert normwise_err(out_s.cpu().numpy(), ref_s) <= TOL_EXPERT
+
+
+# ------------------------------------------------------------------ dense GEMV (output head)
+
+DENSE_CASES = [
+    # fmt, rows, cols, T, seed, scales, sampled: the 4-bit head over the 150,144-token vocabulary,
+    # one token, a batch, and 11 tokens (two batches of at most 8); other shapes take the
+    # runtime-shape kernel
+    (1, 150144, 2048, 1, 70, "narrow", True),
+    (1, 150144, 2048, 5, 71, "full", True),
+    (2, 150144, 2048, 11, 72, "narrow", True),
+    (3, 150144, 2048, 2, 73, "full", True),
+    (1, 1000, 3840, 3, 74, "narrow", False),
+    (2, 777, 192, 9, 75, "full", False),
+    (3, 33, 256, 1, 76, "narrow", False),
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,T,seed,scales,sampled", DENSE_CASES)
+def test_dense_gemv(fmt, rows, cols, T, seed, scales, sampled):
+    """Dense 4-bit GEMV against the oracle: every output within an fp32
+    dot-product bound (2^-14 of sum |w x|) of the float64 value, on sampled
+    rows at the head shape, on every row otherwise."""
+    print("dense", fmt, rows, cols, T, seed, scales, flush=True)
+    mat = synth.make_matrix(fmt, 2, rows, cols, seed, DEV, scale_range=scales)
+    x = synth.make_tokens(T, cols, seed, DEV)
+    out = torch.empty((T, rows), dtype=torch.float32, device=DEV)
+    moe.moe_dense_w4a16_gemv(mat, 1, x, T, out)
+    sync()
+    rng = np.random.default_rng(seed)
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 600, replace=False)])) if sampled \
+        else np.arange(rows)
+    host = synth.matrix_to_numpy(mat, experts={1})
+    xb = bits_of(x)
+    ref = oracle.dense_gemv(host, 1, xb, rows=sel)
+    absw = np.abs(oracle.dequant_matrix(host, 1, sel))
+    bound = 2.0 ** -14 * (np.abs(oracle.bf16_bits_to_f64(xb)) @ absw.T)
+    got = out.cpu().numpy()[:, sel].astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    assert normwise_err(got, ref) <= 1e-5
 
 
 # ------------------------------------------------------------------ combine

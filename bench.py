@@ -227,19 +227,16 @@ def chain_entry(c, fmt_name, K, W, cpu_seconds):
     layers = c.copies(fmt_name, NL)
     NX = max(K, W, 1)
     r0 = [synth.make_tokens(T, H, synth.seed_of(4, i), c.dev) for i in range(NX)]
-    rs = [t.empty((T, H), dtype=t.bfloat16, device=c.dev) for _ in range(NL)]
-    xn = t.empty((T, H), dtype=t.bfloat16, device=c.dev)
-    ids = [t.empty((T, K_TOP), dtype=t.int32, device=c.dev) for _ in range(NL)]
-    ws_ = [t.empty((T, K_TOP), dtype=t.float32, device=c.dev) for _ in range(NL)]
-    nws = moe.moe_layer_decode_workspace_size(layers[0][1], T)
+    ll = moe.LayerList([L for _, L in layers])
+    r_out = t.empty((T, H), dtype=t.bfloat16, device=c.dev)
+    ids_all = t.empty((NL, T, K_TOP), dtype=t.int32, device=c.dev)
+    w_all = t.empty((NL, T, K_TOP), dtype=t.float32, device=c.dev)
+    nws = moe.moe_decode_step_workspace_size(ll, T)
     wsb = t.zeros(nws, dtype=t.uint8, device=c.dev)
+    ids = [ids_all[l] for l in range(NL)]
 
     def step(i, s):
-        r = r0[i % NX]
-        for l in range(NL):
-            moe.moe_rms_norm(r, T, H, CHAIN_EPS, xn, stream=s)
-            moe.moe_layer_decode(layers[l][1], xn, r, T, rs[l], ids[l], ws_[l], wsb, nws, stream=s)
-            r = rs[l]
+        moe.moe_decode_step(ll, r0[i % NX], T, CHAIN_EPS, r_out, None, ids_all, w_all, wsb, nws, stream=s)
 
     ms = c.timed(step, K, W)
     ms_step = ms / K
@@ -252,7 +249,8 @@ def chain_entry(c, fmt_name, K, W, cpu_seconds):
              "expert_bytes_per_step": bytes_step, "resident_weight_bytes": NL * (E + 1) * eb,
              "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                          "kernel": "47 x (k_rms_norm + moe_layer_decode), one step, events on the launch stream"},
+                          "kernel": "moe_decode_step: 47 x (k_rms_norm + the three decode launches), one "
+                                    "call per step, events on the launch stream"},
              "cpu_baseline": None}
     if cpu_seconds > 0:
         import oracle

@@ -30,6 +30,7 @@ EXPORTED = [
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_ffn_workspace_size",
     "moe_grouped_w4a16_ffn", "moe_combine", "moe_layer_decode_workspace_size", "moe_layer_decode",
     "moe_rms_norm", "moe_layer_decode_noalloc_max_bytes", "moe_layer_decode_noalloc", "moe_dense_w4a16_gemv",
+    "moe_decode_step_workspace_size", "moe_decode_step",
 ]
 
 
@@ -77,6 +78,8 @@ def _load():
         "moe_rms_norm": (I, [P, I, I, ctypes.c_float, P, S]),
         "moe_layer_decode_noalloc_max_bytes": (Z, []),
         "moe_dense_w4a16_gemv": (I, [ctypes.POINTER(W4Matrix), I, P, I, P, S]),
+        "moe_decode_step_workspace_size": (Z, [ctypes.POINTER(LayerWeights), I, I, I]),
+        "moe_decode_step": (I, [ctypes.POINTER(LayerWeights), I, P, I, ctypes.c_float, P, P, P, P, P, Z, S]),
         "moe_layer_decode_noalloc": (I, [ctypes.POINTER(LayerWeights), P, P, I, P, P, P, S]),
     }
     for name, (res, args) in sig.items():
@@ -210,3 +213,26 @@ def moe_layer_decode_noalloc(layer, x, residual, T, y, ids_out=None, w_out=None,
 def moe_dense_w4a16_gemv(mat, expert, x, T, out, stream=None):
     m = w4_matrix(mat)
     return _check(_lib.moe_dense_w4a16_gemv(ctypes.byref(m), int(expert), _ptr(x), T, _ptr(out), _stream(stream)))
+
+
+class LayerList:
+    """A host array of moe_layer_weights for moe_decode_step (keeps the layers alive)."""
+
+    def __init__(self, layers):
+        self.layers = [l if isinstance(l, Layer) else Layer(l) for l in layers]
+        self.arr = (LayerWeights * len(self.layers))(*[l.c for l in self.layers])
+
+    def __len__(self):
+        return len(self.layers)
+
+
+def moe_decode_step_workspace_size(layers, T, with_r_all=False):
+    ll = layers if isinstance(layers, LayerList) else LayerList(layers)
+    return _lib.moe_decode_step_workspace_size(ll.arr, len(ll), T, int(bool(with_r_all)))
+
+
+def moe_decode_step(layers, r_in, T, eps, r_out, r_all=None, ids_out=None, w_out=None, ws=None, ws_bytes=0,
+                    stream=None):
+    ll = layers if isinstance(layers, LayerList) else LayerList(layers)
+    return _check(_lib.moe_decode_step(ll.arr, len(ll), _ptr(r_in), T, float(eps), _ptr(r_out), _ptr(r_all),
+                                       _ptr(ids_out), _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))

@@ -424,6 +424,78 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
   return layer_decode_on(L, x, residual, T, y, ids_out, w_out, ws, stream);
 }
 
+// ---- the chained decode step: norm + layer for every layer, one call
+static bool same_shape(const moe_layer_weights& a, const moe_layer_weights& b) {
+  const int ia = a.shared ? a.shared->gate.rows : 0, ib = b.shared ? b.shared->gate.rows : 0;
+  return a.H == b.H && a.I == b.I && a.E == b.E && a.k == b.k && ia == ib &&
+         a.experts.gate.fmt == b.experts.gate.fmt;
+}
+
+static size_t step_ws(const moe_layer_weights* layers, int T, bool own_r, size_t* layer_bytes) {
+  const size_t lb = align256(decode_ws(&layers[0], T, nullptr, nullptr));
+  const size_t tok = align256((size_t)T * layers[0].H * sizeof(uint16_t));
+  if (layer_bytes) *layer_bytes = lb;
+  return lb + tok * (own_r ? 3 : 1);
+}
+
+static int check_step(const moe_layer_weights* layers, int n_layers, const char* who) {
+  if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "%s: need at least one layer", who);
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = check_layer(&layers[l], who);
+    if (rc) return rc;
+    if (!same_shape(layers[0], layers[l]))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d differs in shape or format from layer 0", who, l);
+  }
+  return MOE_OK;
+}
+
+size_t moe_decode_step_workspace_size(const moe_layer_weights* layers, int n_layers, int T, int with_r_all) {
+  if (T < 0 || check_step(layers, n_layers, "moe_decode_step_workspace_size")) return 0;
+  return step_ws(layers, T, !with_r_all, nullptr);
+}
+
+int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_t* r_in, int T, float eps,
+                    uint16_t* r_out, uint16_t* r_all, int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_step(layers, n_layers, "moe_decode_step");
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: T=%d < 0", T);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: eps must be finite, >= 0");
+  if (!r_in || !r_out) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: null r_in or r_out");
+  if ((ids_out == nullptr) != (w_out == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: ids_out and w_out must both be given or both be NULL");
+  if (!aligned16(r_in) || !aligned16(r_out) || (r_all && !aligned16(r_all)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: r_in / r_out / r_all must be 16-byte aligned");
+  size_t lb = 0;
+  const size_t need = step_ws(layers, T, r_all == nullptr, &lb);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))
+    return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: workspace %zu < %zu bytes or not 256-byte aligned", ws_bytes,
+                need);
+  if (T == 0) return MOE_OK;
+  const int H = layers[0].H, k = layers[0].k;
+  const size_t tok = align256((size_t)T * H * sizeof(uint16_t));
+  char* base = (char*)ws;
+  uint16_t* x = (uint16_t*)(base + lb);
+  uint16_t* ping[2] = {(uint16_t*)(base + lb + tok), (uint16_t*)(base + lb + 2 * tok)};
+  hipStream_t s = as_stream(stream);
+  const uint16_t* r = r_in;
+  for (int l = 0; l < n_layers; ++l) {
+    uint16_t* next = l == n_layers - 1 ? r_out : r_all ? r_all + (size_t)l * T * H : ping[l & 1];
+    rc = hip_status(moe::launch_rms_norm(r, T, H, eps, x, s), "moe_decode_step");
+    if (rc) return rc;
+    rc = layer_decode_on(&layers[l], x, r, T, next, ids_out ? ids_out + (size_t)l * T * k : nullptr,
+                         w_out ? w_out + (size_t)l * T * k : nullptr, base, stream);
+    if (rc) return rc;
+    if (r_all && l == n_layers - 1) {
+      rc = hip_status(hipMemcpyAsync(r_all + (size_t)l * T * H, r_out, (size_t)T * H * sizeof(uint16_t),
+                                     hipMemcpyDeviceToDevice, s), "moe_decode_step");
+      if (rc) return rc;
+    }
+    r = next;
+  }
+  return MOE_OK;
+}
+
 size_t moe_layer_decode_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
 
 int moe_layer_decode_noalloc(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,

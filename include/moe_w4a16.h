@@ -248,6 +248,28 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
                      int T, uint16_t* y, int32_t* ids_out, float* w_out,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step through n_layers chained MoE layers (the 47 MoE layers of
+ * "Recursive Flint: 40B Local Coding Model, Benchmarks", section "What is
+ * Recursive Flint?"), issued as one call:
+ *   r_0 = r_in;  for l < n_layers:  x_l = moe_rms_norm(r_l, eps),
+ *                r_{l+1} = moe_layer_decode(layers[l], x_l, residual = r_l);
+ *   r_out = r_{n_layers}.
+ * The norms between the layers are not on the pages: the gain-free RMS
+ * normalisation stands in for them (see moe_rms_norm), so every layer's
+ * routing depends on the layer before.  layers: host array of n_layers
+ * layer descriptors of one shape and format (one workspace serves all).
+ * r_in, r_out bf16 [T, H]; r_all bf16 [n_layers, T, H] or NULL receives
+ * r_1 .. r_{n_layers}; ids_out int32 [n_layers, T, k] and w_out fp32
+ * [n_layers, T, k] may be NULL (both or neither).  Workspace:
+ * moe_decode_step_workspace_size(layers, n_layers, T, r_all != NULL) bytes,
+ * 256-byte aligned, zero-filled before its first use (it holds a layer
+ * workspace).  The result equals the same sequence of moe_rms_norm and
+ * moe_layer_decode calls bit for bit. */
+size_t moe_decode_step_workspace_size(const moe_layer_weights* layers, int n_layers, int T, int with_r_all);
+int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_t* r_in, int T, float eps,
+                    uint16_t* r_out, uint16_t* r_all, int32_t* ids_out, float* w_out, void* ws,
+                    size_t ws_bytes, void* stream);
+
 /* moe_layer_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation).  Same kernels, numerics and

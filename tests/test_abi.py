@@ -164,3 +164,25 @@ def test_layer_decode_noalloc_validation():
     assert moe.moe_layer_decode_workspace_size(big, 64) > cap
     msg = expect(uns, moe.moe_layer_decode_noalloc, big, FAKE, None, 64, FAKE)
     assert "scratch" in msg
+
+
+def test_decode_step_validation():
+    """One call for a chain of layers: every layer must share layer 0's shape and
+    format (one workspace serves them all), and the usual argument checks run
+    before anything is launched."""
+    inv = moe.MOE_ERR_INVALID_ARG
+    mk = lambda **kw: dict({"H": 256, "I": 128, "E": 4, "k": 2, "w_router": FAKE, "experts": fake_ffn(),
+                            "shared": fake_ffn(E=1)}, **kw)
+    layers = [mk(), mk(), mk()]
+    need = moe.moe_decode_step_workspace_size(layers, 8)
+    need_all = moe.moe_decode_step_workspace_size(layers, 8, with_r_all=True)
+    assert need > need_all > 0
+    assert moe.moe_decode_step(layers, FAKE, 0, 1e-6, FAKE, ws=FAKE, ws_bytes=need) == 0
+    expect(inv, moe.moe_decode_step, layers, FAKE, 8, 1e-6, FAKE, ws=FAKE, ws_bytes=need - 1)
+    expect(inv, moe.moe_decode_step, layers, FAKE, 8, -1.0, FAKE, ws=FAKE, ws_bytes=need)
+    expect(inv, moe.moe_decode_step, layers, FAKE, 8, 1e-6, None, ws=FAKE, ws_bytes=need)
+    expect(inv, moe.moe_decode_step, layers, FAKE, 8, 1e-6, FAKE, ids_out=FAKE, ws=FAKE, ws_bytes=need)
+    odd = [mk(), mk(k=1), mk()]
+    msg = expect(inv, moe.moe_decode_step, odd, FAKE, 8, 1e-6, FAKE, ws=FAKE, ws_bytes=need)
+    assert "layer 1" in msg
+    expect(inv, moe.moe_decode_step, [mk(), mk(shared=None)], FAKE, 8, 1e-6, FAKE, ws=FAKE, ws_bytes=need)

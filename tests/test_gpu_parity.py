@@ -552,6 +552,52 @@ def test_chain_teacher_forced(fmt):
     assert prev_ids is not None
 
 
+@pytest.mark.parametrize("fmt,T,NL", [(1, 8, 3), (2, 8, 2), (1, 1, 2)])
+def test_decode_step_matches_calls_and_oracle(fmt, T, NL):
+    """moe_decode_step (one call for NL chained layers) equals the same
+    moe_rms_norm + moe_layer_decode calls bit for bit, and every layer of it,
+    fed the GPU's own residual (teacher forcing), passes the layer checks."""
+    print("decode step", fmt, T, NL, flush=True)
+    H, I, E, k, eps = 2048, 768, 256, 6, 1e-6
+    layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(40, l), DEV) for l in range(NL)]
+    ll = moe.LayerList(layers)
+    r0 = synth.make_tokens(T, H, 41, DEV)
+    nws = moe.moe_decode_step_workspace_size(ll, T, with_r_all=True)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=DEV)
+    r_out = torch.empty_like(r0)
+    r_all = torch.empty((NL, T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((NL, T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((NL, T, k), dtype=torch.float32, device=DEV)
+    moe.moe_decode_step(ll, r0, T, eps, r_out, r_all, ids, w, ws, nws)
+    # the same chain through the separate calls
+    r = r0
+    nws1 = moe.moe_layer_decode_workspace_size(ll.layers[0], T)
+    ws1 = torch.zeros(nws1, dtype=torch.uint8, device=DEV)
+    xs = []
+    for l in range(NL):
+        x = torch.empty_like(r)
+        moe.moe_rms_norm(r, T, H, eps, x)
+        y = torch.empty_like(r)
+        moe.moe_layer_decode(ll.layers[l], x, r, T, y, None, None, ws1, nws1)
+        xs.append(x)
+        r = y
+    sync()
+    assert torch.equal(r.view(torch.int16), r_out.view(torch.int16))
+    assert torch.equal(r_all[NL - 1].view(torch.int16), r_out.view(torch.int16))
+    # teacher forcing: layer l on the GPU's r_l
+    r = r0
+    for l in range(NL):
+        check_layer(layers[l], xs[l], r, r_all[l], ids[l], w[l])
+        r = r_all[l]
+    # a step without r_all gives the same result
+    nws2 = moe.moe_decode_step_workspace_size(ll, T)
+    ws2 = torch.zeros(nws2, dtype=torch.uint8, device=DEV)
+    r_out2 = torch.empty_like(r0)
+    moe.moe_decode_step(ll, r0, T, eps, r_out2, None, None, None, ws2, nws2)
+    sync()
+    assert torch.equal(r_out2.view(torch.int16), r_out.view(torch.int16))
+
+
 def test_rms_norm_in_place_and_ranges():
     """The normalisation kernel in place (x == r), on rows of very
     different scales, against the oracle within one bf16 ulp."""

@@ -21,6 +21,9 @@ a group-64 affine INT4 build.  The readings taken here:
   4-bit groups): weight = fp16 scale * q + fp16 bias, q in 0..15, one
   (scale, bias) per 64 consecutive elements along the reduction axis.  The
   zero-point form is the special case bias = -scale * z.
+* BF16 weights (the 16-bit checkpoint that "[Model] Add Flint
+  (RecursiveSI/flint)", section "What happened", serves beside NVFP4):
+  ``codes`` holds the bf16 bit patterns [E, rows, cols] themselves.
 * A matrix is stored row-major as [out, in]; element 2i of a row sits in
   the low nibble of byte i, element 2i+1 in the high nibble.
 
@@ -37,6 +40,7 @@ import numpy as np
 FMT_NVFP4 = 1
 FMT_INT4_G64 = 2
 FMT_INT4_SB = 3
+FMT_BF16 = 4
 NVFP4_BLOCK = 16
 INT4_GROUP = 64
 
@@ -95,6 +99,8 @@ def dequant_matrix(mat, expert, rows=None):
         if mat.get(key) is not None:
             sub[key] = {expert: _rows(mat[key][expert], rows)}
     mat = sub
+    if mat["fmt"] == FMT_BF16:
+        return bf16_bits_to_f64(mat["codes"][expert])
     q = unpack_nibbles(mat["codes"][expert])
     rows, cols = q.shape
     if mat["fmt"] == FMT_NVFP4:
@@ -122,7 +128,7 @@ def dequant_matrix_f32(mat, expert):
 
     For NVFP4, block scale * code has at most 6 significant bits, so the
     float64 product with the fp32 tensor scale is exact and this is a single
-    rounding of the true value.  INT4 zero-point weights (at most 15
+    rounding of the true value (bf16 weights are exact).  INT4 zero-point weights (at most 15
     significant bits) are exact in float32; scale + bias weights are exact in
     float64, so this is again one rounding of the true value.
     """

@@ -198,3 +198,16 @@ def test_dequant_int4_scale_bias_f32_is_one_rounding():
     ref = torch.from_numpy(exact).to(torch.float32).numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     assert np.any(ref.astype(np.float64) != exact)      # some sums really round
+
+
+def test_dequant_bf16_weights_are_the_bit_patterns():
+    # BF16 weights: the codes are bf16 bit patterns; the dequantised matrix is their value,
+    # as torch's bfloat16 -> float64 conversion gives it (all 65536 patterns, NaN excepted)
+    bits = np.arange(65536, dtype=np.uint16).reshape(1, 256, 256)
+    mat = {"fmt": 4, "codes": bits, "scales": None, "zeros": None, "tensor_scale": None}
+    w = oracle.dequant_matrix(mat, 0)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(w[ok], ref[ok]) and np.array_equal(np.isnan(w), np.isnan(ref))
+    # a row subset
+    assert np.array_equal(oracle.dequant_matrix(mat, 0, [3, 1]), w[[3, 1]])

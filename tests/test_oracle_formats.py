@@ -206,7 +206,7 @@ def test_dequant_bf16_weights_are_the_bit_patterns():
     bits = np.arange(65536, dtype=np.uint16).reshape(1, 256, 256)
     mat = {"fmt": 4, "codes": bits, "scales": None, "zeros": None, "tensor_scale": None}
     w = oracle.dequant_matrix(mat, 0)
-    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ref = torch.from_numpy(bits[0].astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     ok = ~np.isnan(ref)
     assert np.array_equal(w[ok], ref[ok]) and np.array_equal(np.isnan(w), np.isnan(ref))
     # a row subset

@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="all")
-    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4", "int4sb"])
+    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "int4", "int4sb", "bf16"])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the headline's CPU oracle leg")
     p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, -1, -2, -3
-MOE_FMT_NVFP4, MOE_FMT_INT4_G64, MOE_FMT_INT4_SB = 1, 2, 3
+MOE_FMT_NVFP4, MOE_FMT_INT4_G64, MOE_FMT_INT4_SB, MOE_FMT_BF16 = 1, 2, 3, 4
 MOE_MODE_AUTO, MOE_MODE_GEMV, MOE_MODE_MFMA = 0, 1, 2
 
 EXPORTED = [

@@ -25,6 +25,12 @@ namespace moe {
 constexpr int kFmtNvfp4 = 1;
 constexpr int kFmtInt4 = 2;
 constexpr int kFmtInt4Sb = 3;  // INT4 with scale and bias per group of 64
+constexpr int kFmtBf16 = 4;    // 16-bit weights, no quantisation
+// Weights per GEMV piece (one 16-byte load of a row): 32 four-bit codes, or 8
+// bf16 weights (one 16-byte chunk of a staged token piece).
+constexpr int piece_w(int fmt) { return fmt == kFmtBf16 ? 8 : 32; }
+// Token staging layout: the INT4 forms stage permuted chunks plus piece sums.
+constexpr bool int_layout(int fmt) { return fmt == kFmtInt4 || fmt == kFmtInt4Sb; }
 
 MOE_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 

@@ -37,7 +37,7 @@ struct Piece64 {
 // Store one piece (chunks at a stride of `np` 16-byte chunks) in the FMT layout.
 template <int FMT>
 MOE_DEV void store_piece(uint4* __restrict__ dst, int np, float* __restrict__ dsum, const Piece64& v) {
-  if (FMT == kFmtNvfp4) {
+  if (!int_layout(FMT)) {
     dst[0] = v.a;
     dst[np] = v.b;
     dst[2 * np] = v.c;
@@ -106,7 +106,9 @@ MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t
                             const uint8_t* __restrict__ zeros_row, int p) {
   RawPiece r;
   r.c = *(const uint4*)(codes_row + 16 * p);
-  if (FMT == kFmtNvfp4) {
+  if (FMT == kFmtBf16) {
+    r.s = r.z = 0;
+  } else if (FMT == kFmtNvfp4) {
     r.s = *(const uint16_t*)(scales_row + 2 * p);
     r.z = 0;
   } else {
@@ -123,6 +125,25 @@ MOE_DEV RawPiece load_piece(const uint8_t* __restrict__ codes_row, const uint8_t
 template <int FMT, int NT>
 MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs, int xstride,
                        const float* __restrict__ xsum, int sstride, int nt, float (&acc)[NT]) {
+  if constexpr (FMT == kFmtBf16) {
+    // piece p = 8 weights = chunk p % 4 of staged token piece p / 4
+    const int pp = p >> 2, cc = p & 3;
+    const moe_bf16x2 w0 = __builtin_bit_cast(moe_bf16x2, r.c.x), w1 = __builtin_bit_cast(moe_bf16x2, r.c.y);
+    const moe_bf16x2 w2 = __builtin_bit_cast(moe_bf16x2, r.c.z), w3 = __builtin_bit_cast(moe_bf16x2, r.c.w);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nt) {
+        const uint4 xv = ((const uint4*)(xs + t * xstride))[cc * sstride + pp];
+        float d = 0.f;
+        d = dot2_bf16(w0, xv.x, d);
+        d = dot2_bf16(w1, xv.y, d);
+        d = dot2_bf16(w2, xv.z, d);
+        d = dot2_bf16(w3, xv.w, d);
+        acc[t] += d;
+      }
+    }
+    return;
+  }
   moe_bf16x2 q[16];
   float b0, b1, zc = 0.f;
   const uint4 c = r.c;
@@ -195,8 +216,9 @@ struct MatDev {
   int rows, cols;
 };
 
+template <int FMT>
 MOE_DEV const uint8_t* row_codes(const MatDev& m, int e, int r) {
-  return m.codes + ((size_t)e * m.rows + r) * (size_t)(m.cols / 2);
+  return m.codes + ((size_t)e * m.rows + r) * (size_t)(FMT == kFmtBf16 ? m.cols * 2 : m.cols / 2);
 }
 template <int FMT>
 MOE_DEV const uint8_t* row_scales(const MatDev& m, int e, int r) {

@@ -25,8 +25,21 @@ __global__ void __launch_bounds__(256) k_dequant_dev_ts(int fmt, int rows, int c
   if (w >= (long long)rows * words_per_row) return;
   const int r = (int)(w / words_per_row);
   const int c0 = (int)(w % words_per_row) * 8;
-  const uint32_t word = *(const uint32_t*)(codes + (size_t)r * (cols / 2) + c0 / 2);
   float v[8];
+  if (fmt == kFmtBf16) {
+    const uint4 b = *(const uint4*)(codes + ((size_t)r * cols + c0) * 2);
+    const uint32_t h[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(h[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(h[i] >> 16);
+    }
+    float4* o = (float4*)(out + (size_t)r * cols + c0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    return;
+  }
+  const uint32_t word = *(const uint32_t*)(codes + (size_t)r * (cols / 2) + c0 / 2);
   if (fmt == kFmtNvfp4) {
     const uint8_t sb = ((const uint8_t*)scales)[(size_t)r * (cols / 16) + c0 / 16];
     const float b = e4m3_to_f32(sb, 0);

@@ -30,7 +30,7 @@ struct DenseArgs {
 template <int FMT, int PCL>
 MOE_DEV void dense_load(const DenseArgs& g, int n, int lir, int lpr, int ppl, int q0, RawPiece (&r)[PCL]) {
   const int nc = min(n, g.rows - 1);  // a lane group past the last row loads the last row (unused)
-  const uint8_t* rc = row_codes(g.m, g.e, nc);
+  const uint8_t* rc = row_codes<FMT>(g.m, g.e, nc);
   const uint8_t* rs = row_scales<FMT>(g.m, g.e, nc);
   const uint8_t* rz = row_zeros<FMT>(g.m, g.e, nc);
 #pragma unroll
@@ -144,6 +144,7 @@ int dense_max_tokens() { return kDenseNT; }
 
 hipError_t launch_dense_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
                              hipStream_t s) {
+  if (m->fmt == kFmtBf16) return hipErrorInvalidValue;  // 4-bit formats only
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;

@@ -117,8 +117,8 @@ MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, 
     const int i = row0 + row_step * (c / ppl);
     if (c < npc && i < i1) {
       const int p = lir + (c % ppl) * lpr;
-      rg[q] = load_piece<FMT>(row_codes(G, e, i), row_scales<FMT>(G, e, i), row_zeros<FMT>(G, e, i), p);
-      ru[q] = load_piece<FMT>(row_codes(U, e, i), row_scales<FMT>(U, e, i), row_zeros<FMT>(U, e, i), p);
+      rg[q] = load_piece<FMT>(row_codes<FMT>(G, e, i), row_scales<FMT>(G, e, i), row_zeros<FMT>(G, e, i), p);
+      ru[q] = load_piece<FMT>(row_codes<FMT>(U, e, i), row_scales<FMT>(U, e, i), row_zeros<FMT>(U, e, i), p);
     }
   }
 }
@@ -139,7 +139,7 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
   const int H = FIX ? 32 * KP : H_rt;
   const int lpr = FIX ? LPR : lpr_rt;
   const int rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
-  const int ppl = (H / 32) / lpr;
+  const int ppl = (H / piece_w(FMT)) / lpr;
   const int iters = FIX ? 1 : (i1 - i0 + 4 * rpw - 1) / (4 * rpw);  // row iterations per wave
   const int npc = iters * ppl;                                       // pieces per lane per matrix
   uint16_t* xs = (uint16_t*)smem;
@@ -214,7 +214,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
   const int K = FIX ? 32 * KP : D.cols, H = D.rows;
   const int lpr = FIX ? LPR : lpr_rt;
   const int rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
-  const int ppl = (K / 32) / lpr;
+  const int ppl = (K / piece_w(FMT)) / lpr;
   const int iters = FIX ? 1 : (n1 - n0 + 4 * rpw - 1) / (4 * rpw);
   const int npc = iters * ppl;
   uint16_t* xs = (uint16_t*)smem;
@@ -228,7 +228,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
 #pragma unroll
     for (int q = 0; q < PC; ++q) {
       const int n = FIX ? row0 : row0 + 4 * rpw * (q / ppl);
-      if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
+      if (q < npc && n < n1) rd[q] = load_piece<FMT>(row_codes<FMT>(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
                                                       lir + (FIX ? q : q % ppl) * lpr);
     }
   }
@@ -247,7 +247,7 @@ MOE_DEV void down_rows(const MatDev& D, int e, int r0, int r1, int n0, int n1, c
           const int c = c0 + q;
           const int n = row0 + 4 * rpw * (c / ppl);
           if (c < npc && n < n1)
-            rd[q] = load_piece<FMT>(row_codes(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
+            rd[q] = load_piece<FMT>(row_codes<FMT>(D, e, n), row_scales<FMT>(D, e, n), row_zeros<FMT>(D, e, n),
                                     lir + (c % ppl) * lpr);
         }
       }
@@ -648,7 +648,7 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   __syncthreads();
   constexpr int LPR_C = down_lpr(1, IP);
   const int lpr = IP ? LPR_C : a.lpr_i, rpw = 64 / lpr, lir = lane % lpr, rsub = lane / lpr;
-  const int ppl = IP ? IP / LPR_C : (I / 32) / lpr;
+  const int ppl = IP ? IP / LPR_C : (I / piece_w(FMT)) / lpr;
   const int d = wave * rpw + rsub;  // this lane group's row-dot: unit d / R, row n0 + d % R
   const int u = d / R, n = n0 + d % R;
   const bool active = u < nu && n < H;
@@ -674,7 +674,7 @@ __global__ void __launch_bounds__(kT1Threads) k_layer_down_t1(LayerArgs a) {
   if (hp1 < total) hv1 = h_piece(hp1);
   RawPiece rd[kMaxPcD];
   {
-    const uint8_t* rc = row_codes(D, e, nc);
+    const uint8_t* rc = row_codes<FMT>(D, e, nc);
     const uint8_t* rs = row_scales<FMT>(D, e, nc);
     const uint8_t* rz = row_zeros<FMT>(D, e, nc);
 #pragma unroll
@@ -836,8 +836,9 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   g.out = out;
   g.slices_r = (I + kRG - 1) / kRG;
   g.slices_d = (H + kRD - 1) / kRD;
-  g.lpr_h = std::min(lanes_per_row(H), kLprTokens);
-  g.lpr_i = std::min(lanes_per_row(I), kLprDownTokens);
+  const int pw = piece_w(w->gate.fmt);
+  g.lpr_h = lanes_for(H / pw, kLprTokens);
+  g.lpr_i = lanes_for(I / pw, kLprDownTokens);
   constexpr int NT = 8;
   const size_t lds = std::max((size_t)NT * H * 2 + (size_t)NT * (H / 32) * 4,
                               (size_t)NT * I * 2 + (size_t)NT * (I / 32) * 4);
@@ -847,6 +848,9 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   } else if (w->gate.fmt == kFmtInt4Sb) {
     hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4Sb, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
     hipLaunchKernelGGL((k_grouped_down<kFmtInt4Sb, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+  } else if (w->gate.fmt == kFmtBf16) {
+    hipLaunchKernelGGL((k_grouped_gateup<kFmtBf16, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    hipLaunchKernelGGL((k_grouped_down<kFmtBf16, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   } else {
     hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
     hipLaunchKernelGGL((k_grouped_down<kFmtInt4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
@@ -858,10 +862,10 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
 // launch 3 is used: the shared expert (if any) must have the routed inter
 // size (its h row shares the staging layout), every unit's row-dots must fit
 // one pass of the block's lane groups, and a lane's pieces its registers.
-static int down_t1_rows(int T, int I, int Is, int k, bool shared) {
+static int down_t1_rows(int T, int I, int Is, int k, bool shared, int pw) {
   if (T != 1 || (shared && Is != I) || k > 8) return 0;
-  const int lpr = std::min(lanes_per_row(I), 64);
-  if ((I / 32) / lpr > kMaxPcD) return 0;
+  const int lpr = lanes_for(I / pw, 64);
+  if ((I / pw) / lpr > kMaxPcD) return 0;
   const int units = k + (shared ? 1 : 0);
   const int rows = (kT1Threads / lpr) / units;
   if (rows < 1 || (size_t)units * I * 2 + (size_t)units * (I / 32) * 4 > 64 * 1024) return 0;
@@ -893,7 +897,7 @@ static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) 
 // registers, 2.6x slower; one INT4 token gains (24.3 -> 21.4 us).
 template <int FMT, int NT>
 static void launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
-  if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && (FMT == kFmtNvfp4 || NT == 1))
+  if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && FMT != kFmtBf16 && (FMT == kFmtNvfp4 || NT == 1))
     launch_all<FMT, NT, 64, 24>(a, lds, s);
   else
     launch_all<FMT, NT, 0, 0>(a, lds, s);
@@ -942,16 +946,21 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.nR = a.nRe * ((T + a.rt - 1) / a.rt);
   a.nsb = L->shared ? (T + NT - 1) / NT : 0;
   // a single token has little work per block: smaller slices spread it over more CUs
-  a.rg = T == 1 ? 4 : kRG;
-  a.rd = T == 1 ? kRDMin : kRD;
+  const bool bf = L->experts.gate.fmt == kFmtBf16;
+  // bf16 weights: 64 lanes per gate/up row (4 pieces of 8 weights per lane at
+  // hidden 2048) and 4 rows per block, 32 down rows per block, so a block's
+  // pieces stay in registers
+  a.rg = (T == 1 || bf) ? 4 : kRG;
+  a.rd = (T == 1 || bf) ? kRDMin : kRD;
   a.ss_r = L->shared ? (a.Is + a.rg - 1) / a.rg : 0;
   a.slices_r = (a.I + a.rg - 1) / a.rg;
   a.slices_d = (a.H + a.rd - 1) / a.rd;
-  a.lpr_h = std::min(lanes_per_row(a.H), NT == 1 ? 64 : kLprTokens);
-  a.lpr_i = std::min(lanes_per_row(a.I), NT == 1 ? 64 : kLprDownTokens);
-  a.lpr_is = a.Is ? std::min(lanes_per_row(a.Is), NT == 1 ? 64 : kLprDownTokens) : 64;
+  const int pw = bf ? 8 : 32;
+  a.lpr_h = lanes_for(a.H / pw, (NT == 1 || bf) ? 64 : kLprTokens);
+  a.lpr_i = lanes_for(a.I / pw, NT == 1 ? 64 : bf ? 32 : kLprDownTokens);
+  a.lpr_is = a.Is ? lanes_for(a.Is / pw, NT == 1 ? 64 : bf ? 32 : kLprDownTokens) : 64;
   a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
-  a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr);
+  a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr, pw);
   a.sync_slices = (a.H + kRDMin - 1) / kRDMin;
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const int fmt = L->experts.gate.fmt;
@@ -959,6 +968,7 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
     constexpr int N = decltype(nt)::value;
     if (fmt == kFmtNvfp4) launch_shape<kFmtNvfp4, N>(a, lds, s);
     else if (fmt == kFmtInt4Sb) launch_shape<kFmtInt4Sb, N>(a, lds, s);
+    else if (fmt == kFmtBf16) launch_shape<kFmtBf16, N>(a, lds, s);
     else launch_shape<kFmtInt4, N>(a, lds, s);
   };
   if (NT == 1) by_fmt(std::integral_constant<int, 1>{});

@@ -60,6 +60,12 @@
  *           form is its special case bias = -scale * zero.  The matrix-core
  *           grouped GEMM takes NVFP4 and INT4 only: scale+bias weights run the
  *           GEMV kernels at every batch size.
+ *   BF16    (fmt 4) unquantised 16-bit weights, the BF16 checkpoint that
+ *           "[Model] Add Flint (RecursiveSI/flint)", section "What happened",
+ *           serves beside the NVFP4 one: codes = bf16 [E, rows, cols] (2 bytes
+ *           per weight), no scales.  The layer and grouped-FFN calls take it
+ *           (GEMV kernels at every batch size); the dense GEMV and the
+ *           matrix-core mode do not.
  *   Gate and up are [I, H], down is [H, I].  H and I must be multiples of 64.
  */
 #ifndef MOE_W4A16_H
@@ -82,7 +88,7 @@ enum {
   MOE_ERR_HIP = -3          /* a HIP launch failed; see moe_last_error() */
 };
 
-enum { MOE_FMT_NVFP4 = 1, MOE_FMT_INT4_G64 = 2, MOE_FMT_INT4_SB = 3 };
+enum { MOE_FMT_NVFP4 = 1, MOE_FMT_INT4_G64 = 2, MOE_FMT_INT4_SB = 3, MOE_FMT_BF16 = 4 };
 enum { MOE_MODE_AUTO = 0, MOE_MODE_GEMV = 1, MOE_MODE_MFMA = 2 };
 
 /* One packed 4-bit matrix stack (host struct, device pointers). */
@@ -91,7 +97,7 @@ typedef struct moe_w4_matrix {
   int num_experts;           /* E of this stack */
   int rows, cols;            /* out, in (cols = reduction axis); cols <= 3840 (the GEMV
                                 kernels stage 8 tokens' rows of cols in 64 KB of LDS) */
-  const uint8_t* codes;      /* [E, rows, cols/2] */
+  const uint8_t* codes;      /* [E, rows, cols/2]; BF16: bf16 [E, rows, cols] */
   const void* scales;        /* NVFP4: uint8 e4m3 [E, rows, cols/16]; INT4, INT4_SB: fp16 [E, rows, cols/64] */
   const uint8_t* zeros;      /* INT4: uint8 [E, rows, cols/64]; else NULL */
   const float* tensor_scale; /* NVFP4: fp32 [E]; else NULL */
@@ -242,7 +248,9 @@ int moe_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, void* 
  * kernels use to hand work to the last block of a group; every call leaves
  * them reset to zero.  Calls sharing a
  * workspace must not run concurrently.  The shared expert must have the
- * same format and hidden size as the routed experts. */
+ * same format and hidden size as the routed experts.  MOE_FMT_BF16 weights:
+ * T = 1 only (T > 1 returns MOE_ERR_UNSUPPORTED; moe_grouped_w4a16_ffn takes
+ * them at any T). */
 size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T);
 int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual,
                      int T, uint16_t* y, int32_t* ids_out, float* w_out,
@@ -264,7 +272,8 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
  * moe_decode_step_workspace_size(layers, n_layers, T, r_all != NULL) bytes,
  * 256-byte aligned, zero-filled before its first use (it holds a layer
  * workspace).  The result equals the same sequence of moe_rms_norm and
- * moe_layer_decode calls bit for bit. */
+ * moe_layer_decode calls bit for bit.  MOE_FMT_BF16 weights: T = 1 only, as
+ * for moe_layer_decode. */
 size_t moe_decode_step_workspace_size(const moe_layer_weights* layers, int n_layers, int T, int with_r_all);
 int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_t* r_in, int T, float eps,
                     uint16_t* r_out, uint16_t* r_all, int32_t* ids_out, float* w_out, void* ws,

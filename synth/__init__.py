@@ -17,6 +17,7 @@ Value recipes (no trained weights exist here; these stand in for them):
                   over the 16 e4m3 codes 0x30..0x3F (values in [0.5, 2));
                   tensor scale ~ U(0.004, 0.008) per (expert, matrix)
   INT4 group 64   codes uniform; fp16 scale ~ U(0.005, 0.02); zero U{0..15}
+  BF16 weights    bf16 ~ N(0, 0.02), about the RMS of the 4-bit recipes
   INT4 scale+bias codes uniform; fp16 scale ~ U(0.005, 0.02); fp16 bias =
                   -scale * U(6.5, 8.5) (groups roughly centred on zero, as a
                   min/max affine quantiser gives them)
@@ -43,7 +44,8 @@ import torch
 FMT_NVFP4 = 1
 FMT_INT4_G64 = 2
 FMT_INT4_SB = 3
-FMT_NAMES = {"nvfp4": FMT_NVFP4, "int4": FMT_INT4_G64, "int4sb": FMT_INT4_SB}
+FMT_BF16 = 4
+FMT_NAMES = {"nvfp4": FMT_NVFP4, "int4": FMT_INT4_G64, "int4sb": FMT_INT4_SB, "bf16": FMT_BF16}
 
 
 def seed_of(*keys):
@@ -66,6 +68,10 @@ def make_matrix(fmt, num_experts, rows, cols, seed, device="cpu", scale_range="n
         raise ValueError("scale_range must be 'narrow' or 'full'")
     E = num_experts
     g = _gen(device, seed, 1)
+    if fmt == FMT_BF16:
+        w = torch.randn((E, rows, cols), dtype=torch.float32, device=device, generator=g) * 0.02
+        return {"fmt": fmt, "num_experts": E, "rows": rows, "cols": cols, "codes": w.to(torch.bfloat16),
+                "scales": None, "zeros": None, "tensor_scale": None}
     codes = torch.randint(0, 256, (E, rows, cols // 2), dtype=torch.uint8, device=device, generator=g)
     if fmt == FMT_NVFP4:
         if scale_range == "full":
@@ -167,13 +173,13 @@ def _np_expert_slice(t, experts):
     if t is None:
         return None
     if experts is None:
-        return t.detach().cpu().numpy() if t.dtype != torch.float16 else bits16(t)
+        return bits16(t) if t.dtype in (torch.float16, torch.bfloat16) else t.detach().cpu().numpy()
     idx = sorted(int(e) for e in experts)
     if not idx:
         return {}
     sel = torch.as_tensor(idx, device=t.device, dtype=torch.long)
     sub = t.index_select(0, sel)
-    arr = bits16(sub) if sub.dtype == torch.float16 else sub.cpu().numpy()
+    arr = bits16(sub) if sub.dtype in (torch.float16, torch.bfloat16) else sub.cpu().numpy()
     return {e: arr[i] for i, e in enumerate(idx)}
 
 
@@ -203,6 +209,8 @@ def matrix_bytes(fmt, rows, cols):
         return n // 2 + n // 16 + 4
     if fmt == FMT_INT4_SB:
         return n // 2 + 2 * (n // 64) + 2 * (n // 64)
+    if fmt == FMT_BF16:
+        return 2 * n
     return n // 2 + 2 * (n // 64) + n // 64
 
 

@@ -102,7 +102,7 @@ def test_grouped_ffn_validation():
     expect(uns, moe.moe_grouped_w4a16_ffn, f, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, mode=7, ws=FAKE,
            ws_bytes=need)
     bad = fake_ffn()
-    bad["up"]["fmt"] = 4
+    bad["up"]["fmt"] = 5
     expect(uns, moe.moe_grouped_w4a16_ffn, bad, 4, 256, 128, FAKE, FAKE, 6, FAKE, 24, FAKE, ws=FAKE, ws_bytes=need)
     mixed = fake_ffn()
     mixed["down"] = fake_matrix(2, 4, 256, 128)
@@ -186,3 +186,20 @@ def test_decode_step_validation():
     msg = expect(inv, moe.moe_decode_step, odd, FAKE, 8, 1e-6, FAKE, ws=FAKE, ws_bytes=need)
     assert "layer 1" in msg
     expect(inv, moe.moe_decode_step, [mk(), mk(shared=None)], FAKE, 8, 1e-6, FAKE, ws=FAKE, ws_bytes=need)
+
+
+def test_bf16_layer_path_takes_one_token():
+    """bf16 expert weights go through the layer calls for a lone token only;
+    several tokens are rejected on the host before any launch (the grouped
+    FFN call still takes them)."""
+    uns = moe.MOE_ERR_UNSUPPORTED
+    bf = lambda: {"H": 256, "I": 128, "E": 4, "k": 2, "w_router": FAKE, "experts": fake_ffn(fmt=4),
+                  "shared": fake_ffn(fmt=4, E=1)}
+    need = moe.moe_layer_decode_workspace_size(bf(), 4)
+    assert need > 0
+    for T in (2, 4, 64, 100):
+        msg = expect(uns, moe.moe_layer_decode, bf(), FAKE, None, T, FAKE, ws=FAKE, ws_bytes=1 << 30)
+        assert "bf16" in msg
+        expect(uns, moe.moe_layer_decode_noalloc, bf(), FAKE, None, T, FAKE)
+        expect(uns, moe.moe_decode_step, [bf(), bf()], FAKE, T, 1e-6, FAKE, ws=FAKE, ws_bytes=1 << 30)
+    assert moe.moe_layer_decode(bf(), FAKE, None, 0, FAKE, ws=FAKE, ws_bytes=need) == 0

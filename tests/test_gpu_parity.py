@@ -75,7 +75,7 @@ def exhaustive_int4_sb(device):
 
 
 @pytest.mark.parametrize("which", ["nvfp4_exhaustive", "int4_exhaustive", "int4sb_exhaustive", "nvfp4_flint",
-                                   "int4_flint", "int4sb_flint"])
+                                   "int4_flint", "int4sb_flint", "bf16_flint"])
 def test_dequant_bit_exact(which):
     print("dequant", which, flush=True)
     if which == "nvfp4_exhaustive":
@@ -85,7 +85,7 @@ def test_dequant_bit_exact(which):
     elif which == "int4sb_exhaustive":
         mat = exhaustive_int4_sb(DEV)
     else:
-        fmt = {"nvfp4": 1, "int4": 2, "int4sb": 3}[which.split("_")[0]]
+        fmt = {"nvfp4": 1, "int4": 2, "int4sb": 3, "bf16": 4}[which.split("_")[0]]
         mat = synth.make_matrix(fmt, 4, 768, 2048, seed=21, device=DEV, scale_range="full")
     host = synth.matrix_to_numpy(mat)
     for e in range(mat["num_experts"]):
@@ -258,7 +258,9 @@ FFN_CASES_FULL = [(1, 2048, 768, 256, 6, 5, 55), (2, 2048, 768, 256, 6, 5, 56), 
                   (3, 2048, 768, 256, 6, 5, 58), (3, 192, 320, 8, 3, 9, 59)]
 FFN_CASES = FFN_CASES + [(3, 2048, 768, 256, 6, 5, 60), (3, 256, 128, 32, 6, 4, 61),
                          # a dense FFN layer as the one-expert call (inter 3840 assumed; the pages give none)
-                         (1, 2048, 3840, 1, 1, 4, 62), (2, 2048, 3840, 1, 1, 8, 63)]
+                         (1, 2048, 3840, 1, 1, 4, 62), (2, 2048, 3840, 1, 1, 8, 63),
+                         # BF16 weights (the 16-bit checkpoint)
+                         (4, 2048, 768, 256, 6, 5, 64), (4, 192, 320, 8, 3, 9, 65)]
 
 
 @pytest.mark.parametrize("fmt,H,I,E,k,T,seed,scales", [c + ("narrow",) for c in FFN_CASES] +
@@ -411,6 +413,9 @@ def check_layer(layer, x, residual, y, ids, w, tokens=None, ws=None):
     return err
 
 
+BF16_MULTI_OFF = pytest.mark.skip(reason="bf16 weights with T > 1: layer path switched off (unexplained memory "
+                                          "fault in a timed T=16 run); the call returns MOE_ERR_UNSUPPORTED")
+
 LAYER_CASES = [
     # name, fmt, H, I, E, k, T, seed, residual
     ("tiny_int4_T4", 2, 256, 128, 32, 6, 4, 0, False),
@@ -445,6 +450,15 @@ LAYER_CASES = [
     ("flint_int4sb_T4", 3, 2048, 768, 256, 6, 4, 26, False),
     ("flint_int4sb_T16", 3, 2048, 768, 256, 6, 16, 27, True),
     ("ragged_int4sb_H192_I320_T1", 3, 192, 320, 8, 6, 1, 28, False),
+    # BF16 weights
+    ("flint_bf16_T1", 4, 2048, 768, 256, 6, 1, 29, True),
+    # several tokens on bf16 weights: the layer call rejects them (the
+    # several-token kernels in this format are switched off after a memory
+    # fault in a timed run whose cause is not found)
+    pytest.param("flint_bf16_T4", 4, 2048, 768, 256, 6, 4, 30, False, marks=BF16_MULTI_OFF),
+    pytest.param("flint_bf16_T16", 4, 2048, 768, 256, 6, 16, 31, True, marks=BF16_MULTI_OFF),
+    pytest.param("tiny_bf16_T64", 4, 256, 128, 32, 6, 64, 32, False, marks=BF16_MULTI_OFF),
+    ("ragged_bf16_H192_I320_T1", 4, 192, 320, 8, 6, 1, 33, True),
 ]
 
 
@@ -860,7 +874,8 @@ def test_prefill_4096_zipf_sampled():
     assert err <= TOL_LAYER
 
 
-@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100), (3, 100)])
+@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100), (3, 100),
+                                   pytest.param(4, 100, marks=BF16_MULTI_OFF)])
 def test_layer_decode_large_batch_uses_grouped_gemm(fmt, T):
     """Above 64 tokens the layer is composed from the separate calls; 70 tokens
     (420 pairs, under two per expert) take the GEMV grouped FFN, 100 and 200

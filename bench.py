@@ -15,9 +15,10 @@ oracle on a bounded sample of the same workload.
 Decode steps rotate over independently seeded weight copies, enough that no
 copy is read again within 512 MB (twice the ~256 MB memory-side cache) of
 weight traffic, and every step gets fresh tokens; the memory-side cache is
-flushed (a 1 GiB copy) before each timed replay.  K steps are captured in
-one HIP graph; one warm replay, then one timed replay between HIP events on
-the launch stream.
+flushed (a 1 GiB read) right before the timed replay.  K steps are captured
+in one HIP graph; after a warm replay, further warm replays worth 50 ms,
+the flush and the timed replay (between HIP events on the launch stream)
+are queued back to back, so the timed steps start on a busy chip.
 
 The sweep also carries the dense 4-bit output-head GEMV (150,144 x 2048,
 1 and 8 tokens).
@@ -50,15 +51,20 @@ H, I, E, K_TOP = 2048, 768, 256, 6
 CHAIN_LAYERS, CHAIN_T, CHAIN_EPS = 47, 8, 1e-6
 ROTATE_BYTES = 512e6      # no weight copy is read again within this much weight traffic
 MAX_COPIES = 48           # about 33 GB of NVFP4 layer copies
+WARM_MS = 50.0            # untimed graph replays queued right before the timed one
 
-# HBM bytes per measured unit (one layer call; the prefill's grouped FFN) from two rocprofv3
-# --pmc runs of the same workload with the current kernels: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
-# the factors that make the counters read 1 GiB each for a plain 1 GiB device copy
-# (profiles/hbm_traffic_counters.md).  Workloads not listed report null.
+# HBM bytes per measured unit (one layer call; the 47-layer chained step; one head GEMV call;
+# the prefill's grouped FFN, routed + shared) from two rocprofv3 --pmc runs of the same workload
+# with the current kernels: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors that make the
+# counters read 1 GiB each for a plain 1 GiB device copy (profiles/hbm_traffic_counters.md).
+# Workloads not listed report null.
 TRAFFIC_BYTES = {
-    ("decode_b1", "nvfp4"): 21.75e6,
-    ("decode_T16", "nvfp4"): 222.9e6,
-    ("prefill", "nvfp4"): 1239.0e6,
+    ("decode_b1", "nvfp4"): 21.49e6,
+    ("decode_T16", "nvfp4"): 221.7e6,
+    ("decode_T64", "nvfp4"): 560.6e6,
+    ("chain_b8", "nvfp4"): 5.90e9,
+    ("dense_head_T1", "nvfp4"): 173.7e6,
+    ("prefill", "nvfp4"): 1236.8e6,
 }
 
 
@@ -73,6 +79,8 @@ def parse():
     p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--tokens", type=int, default=1, help="tokens of the dense_head workload")
+    p.add_argument("--eager", action="store_true",
+                   help="launch the K timed steps directly instead of replaying a captured graph (profiler runs)")
     return p.parse_args()
 
 
@@ -102,14 +110,23 @@ class Ctx:
         self._flush = None
         self._copies = {}
 
-    def flush(self):
-        """Stream 1 GiB through the memory system (evicts the memory-side cache)."""
+    def _flush_buffers(self):
         t = self.torch
         if self._flush is None:
-            self._flush = (t.empty(1 << 29, dtype=t.uint8, device=self.dev),
-                           t.empty(1 << 29, dtype=t.uint8, device=self.dev))
+            self._flush = t.zeros(1 << 27, dtype=t.int64, device=self.dev)  # 1 GiB
+
+    def _flush_async(self):
+        """Read 1 GiB (a sum): evicts the memory-side cache and, unlike a copy, leaves no
+        dirty lines whose write-back would slow the next steps (a 1 GiB copy cost the first
+        three 16-token steps after it 15, 9 and 3 us)."""
+        self._flush_buffers()
+        self._flush_sum = self._flush.sum()
+
+    def flush(self):
+        """Evict the memory-side cache and wait."""
+        t = self.torch
         with t.cuda.stream(self.stream):
-            self._flush[1].copy_(self._flush[0])
+            self._flush_async()
         t.cuda.synchronize()
 
     def copies(self, fmt_name, n):
@@ -128,22 +145,44 @@ class Ctx:
         self.torch.cuda.empty_cache()
 
     def timed(self, body, K, W):
-        """W eager warm-up steps, K steps captured in one graph, one warm replay, a cache
-        flush, then one timed replay between events on the launch stream.  Returns ms."""
+        """W eager warm-up steps, K steps captured in one graph, one warm replay, then warm
+        replays worth WARM_MS, a cache flush and the timed replay between events on the launch
+        stream, queued together (with --eager: the K steps launched directly after a flush).
+        Returns ms."""
         t, s = self.torch, self.stream
         with t.cuda.stream(s):
             for i in range(W):
                 body(i, s)
         t.cuda.synchronize()
+        if self.args.eager:
+            self.flush()
+            ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            with t.cuda.stream(s):
+                ev0.record(s)
+                for i in range(K):
+                    body(i, s)
+                ev1.record(s)
+            t.cuda.synchronize()
+            return ev0.elapsed_time(ev1)
         g = t.cuda.CUDAGraph()
         with t.cuda.graph(g, stream=s):
             for i in range(K):
                 body(i, s)
-        g.replay()
-        t.cuda.synchronize()
-        self.flush()
         ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         with t.cuda.stream(s):
+            ev0.record(s)
+            g.replay()
+            ev1.record(s)
+        t.cuda.synchronize()
+        # warm replays worth >= WARM_MS of work, the cache flush and the timed replay, queued back
+        # to back: the timed replay starts on a chip that has been busy for a while, not after an
+        # idle gap (clocks ramp with load: 20 steps of 64 tokens ran 8% slower per step than 200
+        # steps when timed after a single warm replay)
+        n_warm = max(1, math.ceil(WARM_MS / max(ev0.elapsed_time(ev1), 1e-3)))
+        with t.cuda.stream(s):
+            for _ in range(n_warm):
+                g.replay()
+            self._flush_async()
             ev0.record(s)
             g.replay()
             ev1.record(s)
@@ -248,7 +287,7 @@ def chain_entry(c, fmt_name, K, W, cpu_seconds):
              "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
              "expert_bytes_per_step": bytes_step, "resident_weight_bytes": NL * (E + 1) * eb,
              "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                          "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get(("chain_b8", fmt_name)),
                           "kernel": "moe_decode_step: 47 x (k_rms_norm + the three decode launches), one "
                                     "call per step, events on the launch stream"},
              "cpu_baseline": None}
@@ -391,7 +430,7 @@ def dense_entry(c, fmt_name, T, K, W, cpu_seconds, rows=150144):
              "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
              "weight_copies": R, "matrix_bytes": mb,
              "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                          "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get(("dense_head_T%d" % T, fmt_name)),
                           "kernel": "k_dense_gemv (one call), events on the launch stream",
                           "bytes": "the packed matrix once per batch of up to 8 tokens"},
              "cpu_baseline": None}

@@ -429,8 +429,11 @@ static int check_decode_args(const moe_layer_weights* L, const uint16_t* x, cons
   return MOE_OK;
 }
 
+// norm_r != NULL: x is a buffer that receives rms_norm(norm_r) (eps) first (the
+// chained step; the fused path computes it inside its first launch).
 static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream);
+                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream,
+                           const uint16_t* norm_r = nullptr, float eps = 0.f);
 
 int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T, uint16_t* y,
                      int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
@@ -503,10 +506,10 @@ int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_
   const uint16_t* r = r_in;
   for (int l = 0; l < n_layers; ++l) {
     uint16_t* next = l == n_layers - 1 ? r_out : r_all ? r_all + (size_t)l * T * H : ping[l & 1];
-    rc = hip_status(moe::launch_rms_norm(r, T, H, eps, x, s), "moe_decode_step");
-    if (rc) return rc;
+    // x_l = rms_norm(r_l) is computed by the layer's first launch (or, above the fused
+    // path's batch sizes, by the norm kernel before it)
     rc = layer_decode_on(&layers[l], x, r, T, next, ids_out ? ids_out + (size_t)l * T * k : nullptr,
-                         w_out ? w_out + (size_t)l * T * k : nullptr, base, stream);
+                         w_out ? w_out + (size_t)l * T * k : nullptr, base, stream, r, eps);
     if (rc) return rc;
     if (r_all && l == n_layers - 1) {
       rc = hip_status(hipMemcpyAsync(r_all + (size_t)l * T * H, r_out, (size_t)T * H * sizeof(uint16_t),
@@ -538,7 +541,8 @@ int moe_layer_decode_noalloc(const moe_layer_weights* L, const uint16_t* x, cons
 }
 
 static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream) {
+                           uint16_t* y, int32_t* ids_out, float* w_out, void* ws, void* stream,
+                           const uint16_t* norm_r, float eps) {
   DecodeWs d;
   decode_ws(L, T, ws, &d);
   hipStream_t s = as_stream(stream);
@@ -557,7 +561,12 @@ static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const 
     b.h_shared = d.h_shared;
     b.o_routed = d.o_routed;
     b.o_shared = d.o_shared;
-    return hip_status(moe::launch_layer_decode(L, x, residual, T, y, b, ids_out, w_out, s), "moe_layer_decode");
+    return hip_status(moe::launch_layer_decode(L, x, residual, T, y, b, ids_out, w_out, s, norm_r, eps),
+                      "moe_layer_decode");
+  }
+  if (norm_r) {
+    const int rc = hip_status(moe::launch_rms_norm(norm_r, T, H, eps, const_cast<uint16_t*>(x), s), "moe_decode_step");
+    if (rc) return rc;
   }
   // Larger batches: composed from the separate kernels (route, group, routed experts, the shared expert as
   // one unit, combine).

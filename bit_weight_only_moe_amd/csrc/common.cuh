@@ -235,4 +235,48 @@ MOE_DEV float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Gain-free RMS normalisation of one bf16 row of H values (H % 8 == 0) by one
+// wave: s = sqrt(mean(r^2) + eps) with the squares summed in a fixed order
+// (lane l takes the 8-element chunks l, l + 64, ... in element order, then a
+// wave sum), q = 1 / s (rounded once), and x = bf16_RNE(r * q) per element.
+// Every caller (the norm kernel, the chained step's first decode launch) goes
+// through these functions, so they agree bit for bit.
+MOE_DEV float rms_scale_wave(const uint16_t* __restrict__ r, int H, float eps, int lane) {
+  const uint4* rr = (const uint4*)r;
+  float ss = 0.f;
+  for (int i = lane; i < H / 8; i += 64) {
+    const uint4 v = rr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_to_f32(w[q] & 0xffffu), b = bf16_to_f32(w[q] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  return 1.0f / sqrtf(wave_sum(ss) / (float)H + eps);
+}
+
+// Two bf16 values (packed) times q, rounded to bf16 (packed).
+MOE_DEV uint32_t rms_apply2(uint32_t w, float q) {
+  return f32_to_bf16_rne(bf16_to_f32(w & 0xffffu) * q) | (f32_to_bf16_rne(bf16_to_f32(w >> 16) * q) << 16);
+}
+
+MOE_DEV uint4 rms_apply8(uint4 v, float q) {
+  return make_uint4(rms_apply2(v.x, q), rms_apply2(v.y, q), rms_apply2(v.z, q), rms_apply2(v.w, q));
+}
+
+// x = rms_norm(r) for one row by one wave, written to dst (and to dst2 when
+// not NULL; either may be LDS or global memory).  A lane writes only the
+// chunks it reads, after the wave's sum, so dst may alias r.
+MOE_DEV void rms_norm_row_wave(const uint16_t* r, int H, float eps, int lane, uint16_t* dst, uint16_t* dst2) {
+  const float s = rms_scale_wave(r, H, eps, lane);
+  const uint4* rr = (const uint4*)r;
+  for (int i = lane; i < H / 8; i += 64) {
+    const uint4 o = rms_apply8(rr[i], s);
+    ((uint4*)dst)[i] = o;
+    if (dst2) ((uint4*)dst2)[i] = o;
+  }
+}
+
 }  // namespace moe

@@ -74,17 +74,29 @@ MOE_DEV Piece64 load_piece64(const uint16_t* __restrict__ src) {
 // piece sums at dsum + t*(K/32).  Each thread takes whole 32-element pieces and issues the
 // loads of two pieces before it writes either, so up to 512 pieces cost one
 // memory round trip.
+//
+// scl (LDS, may be NULL): the rows are RMS-normalised while staged, element
+// v of row t becoming bf16_RNE(v * scl[t]), scl[t] the row's reciprocal root
+// (rms_apply8, the same arithmetic as the normalisation kernel).
 template <int FMT, typename RowOf>
 MOE_DEV void stage_rows(uint16_t* __restrict__ dst, float* __restrict__ dsum, const uint16_t* __restrict__ src,
-                        RowOf row_of, int nt, int K) {
+                        RowOf row_of, int nt, int K, const float* scl = nullptr) {
   const int ppt = K / 32, total = nt * ppt, nthr = blockDim.x;
   for (int p0 = threadIdx.x; p0 < total; p0 += 2 * nthr) {
     const int p1 = p0 + nthr;
     const int t0 = p0 / ppt, t1 = p1 / ppt;
     const int c0 = p0 - t0 * ppt, c1 = p1 - t1 * ppt;
-    const Piece64 v0 = load_piece64(src + (size_t)row_of(t0) * K + 32 * c0);
+    Piece64 v0 = load_piece64(src + (size_t)row_of(t0) * K + 32 * c0);
     Piece64 v1;
     if (p1 < total) v1 = load_piece64(src + (size_t)row_of(t1) * K + 32 * c1);
+    if (scl) {
+      const float s0 = scl[t0];
+      v0 = Piece64{rms_apply8(v0.a, s0), rms_apply8(v0.b, s0), rms_apply8(v0.c, s0), rms_apply8(v0.d, s0)};
+      if (p1 < total) {
+        const float s1 = scl[t1];
+        v1 = Piece64{rms_apply8(v1.a, s1), rms_apply8(v1.b, s1), rms_apply8(v1.c, s1), rms_apply8(v1.d, s1)};
+      }
+    }
     store_piece<FMT>((uint4*)(dst + (size_t)t0 * K) + c0, ppt, dsum + p0, v0);
     if (p1 < total) store_piece<FMT>((uint4*)(dst + (size_t)t1 * K) + c1, ppt, dsum + p1, v1);
   }

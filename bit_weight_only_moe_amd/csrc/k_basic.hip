@@ -394,46 +394,18 @@ hipError_t launch_combine(const float* out_perm, const int32_t* pair_pos, const 
 }
 
 // ---------------------------------------------------------------- chain normalisation
-// x[t] = bf16(r[t] / sqrt(mean_h(r[t]^2) + eps)), one block per token.  Each
-// bf16 square is exact in fp32; a thread sums its squares in ascending
-// column order, the waves' sums are added in wave order, and each element
-// is divided by the rounded root and rounded to bf16 (nearest, ties to
-// even).  Every thread writes only the elements it read, after the block's
-// sum is complete, so x may alias r.
-__global__ void __launch_bounds__(256) k_rms_norm(const uint16_t* r, int H, float eps, uint16_t* x) {
-  __shared__ float part[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint4* rr = (const uint4*)(r + (size_t)blockIdx.x * H);
-  uint4* xx = (uint4*)(x + (size_t)blockIdx.x * H);
-  const int n8 = H / 8;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < n8; i += 256) {
-    const uint4 v = rr[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = bf16_to_f32(w[q] & 0xffffu), b = bf16_to_f32(w[q] >> 16);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) part[wave] = ss;
-  __syncthreads();
-  const float s = sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H + eps);
-  for (int i = threadIdx.x; i < n8; i += 256) {
-    const uint4 v = rr[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = f32_to_bf16_rne(bf16_to_f32(w[q] & 0xffffu) / s) | (f32_to_bf16_rne(bf16_to_f32(w[q] >> 16) / s) << 16);
-    xx[i] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+// x[t] = bf16(r[t] / sqrt(mean_h(r[t]^2) + eps)), one wave per token (four
+// tokens per block).  Each bf16 square is exact in fp32; the sum order, the
+// rounded reciprocal root and the per-element product rounded to bf16
+// (nearest, ties to even) are those of rms_norm_row_wave, which the chained
+// decode step's first launch also uses.  x may alias r.
+__global__ void __launch_bounds__(256) k_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);  // one wave per token
+  if (t < T) rms_norm_row_wave(r + (size_t)t * H, H, eps, threadIdx.x & 63, x + (size_t)t * H, nullptr);
 }
 
 hipError_t launch_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, hipStream_t s) {
-  hipLaunchKernelGGL(k_rms_norm, dim3(T), dim3(256), 0, s, r, H, eps, x);
+  hipLaunchKernelGGL(k_rms_norm, dim3((T + 3) / 4), dim3(256), 0, s, r, T, H, eps, x);
   return hipGetLastError();
 }
 

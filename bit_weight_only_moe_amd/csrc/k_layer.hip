@@ -72,6 +72,11 @@ constexpr int kTicketSlice = 16 * (1 + kMaxBatches);    // + 16 * slice: down un
 struct LayerArgs {
   int T, H, I, Is, E, k;
   const uint16_t* x;
+  // chained step: launch 1 computes x = rms_norm(norm_r) (eps) itself and
+  // writes it to x_w (== x) for launches 2 and 3; NULL: x is given
+  const uint16_t* norm_r;
+  uint16_t* x_w;
+  float eps;
   const uint16_t* residual;
   uint16_t* y;
   const float* w_router;
@@ -123,6 +128,15 @@ MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, 
   }
 }
 
+// Tokens normalised while staged: x_tok = rms_norm(r_tok) (eps).  Used where
+// the rows [r0, r1) are at most 4 tokens (one wave computes each scale);
+// scale: LDS for their 4 scales.  r == NULL: the tokens are staged as given.
+struct NormIn {
+  const uint16_t* r = nullptr;
+  float eps = 0.f;
+  float* scale = nullptr;
+};
+
 // h[r, i] = bf16(silu(gate_e[i] . x_tok(r)) * (up_e[i] . x_tok(r))) for the
 // rows r in [r0, r1) and output rows i in [i0, i1).  tok_of(r): token index.
 // KP > 0: the rows have KP pieces (H = 32 KP) and LPR lanes share a row, both
@@ -133,7 +147,7 @@ MOE_DEV void load_gateup_chunk(const MatDev& G, const MatDev& U, int e, int c0, 
 template <int FMT, int NT, int KP = 0, int LPR = 0, typename TokOf>
 MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1, int i0, int i1, int H_rt,
                          const uint16_t* __restrict__ x, TokOf tok_of, uint16_t* __restrict__ hout, int Iu,
-                         int lpr_rt, uint8_t* smem) {
+                         int lpr_rt, uint8_t* smem, const NormIn& nrm = NormIn{}) {
   constexpr bool FIX = KP > 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = FIX ? 32 * KP : H_rt;
@@ -152,10 +166,17 @@ MOE_DEV void gateup_rows(const MatDev& G, const MatDev& U, int e, int r0, int r1
   RawPiece rg[PC], ru[PC];
   const int row0 = i0 + wave * rpw + rsub;
   if (resident) load_gateup_chunk<FMT, PC>(G, U, e, 0, npc, ppl, lpr, lir, row0, 4 * rpw, i1, rg, ru);
+  // normalised tokens: their scales, one wave per token, with the weight loads in flight
+  if (nrm.r && wave < r1 - r0) {
+    const float sc = rms_scale_wave(nrm.r + (size_t)tok_of(r0 + wave) * H, H, nrm.eps, lane);
+    if (lane == 0) nrm.scale[wave] = sc;
+  }
+  const uint16_t* xsrc = nrm.r ? nrm.r : x;
   for (int rb = r0; rb < r1; rb += NT) {
     const int nt = min(NT, r1 - rb);
     __syncthreads();
-    stage_rows<FMT>(xs, xsum, x, [&](int t) { return tok_of(rb + t); }, nt, H);
+    stage_rows<FMT>(xs, xsum, xsrc, [&](int t) { return tok_of(rb + t); }, nt, H,
+                    nrm.r ? nrm.scale + (rb - r0) : nullptr);
     __syncthreads();
     float ag[NT], au[NT];
 #pragma unroll
@@ -301,9 +322,11 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     const int b = blockIdx.x - a.nR;
     const int slice = b % a.ss_r, r0 = (b / a.ss_r) * NT;
     const int i0 = slice * a.rg, i1 = min(a.Is, i0 + a.rg);
+    __shared__ float s_nscale[4];
+    NormIn nrm;
+    if (a.norm_r) nrm = NormIn{a.norm_r, a.eps, s_nscale};
     gateup_rows<FMT, NT, GP, gate_lpr(NT, GP)>(a.sgate, a.sup, 0, r0, min(T, r0 + NT), i0, i1, H, a.x,
-                                               [](int r) { return r; },
-                         a.h_shared, a.Is, a.lpr_h, smem);
+                                               [](int r) { return r; }, a.h_shared, a.Is, a.lpr_h, smem, nrm);
     return;
   }
   const int nb = a.nR / a.nRe;  // token batches
@@ -315,7 +338,15 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     // a wave past the last expert loads the last expert's row (never used):
     // no branch around the loads, whose registers the token copy then reuses
     router_prefetch(a.w_router + (size_t)min(e, E - 1) * H, H, lane, wv);
-    copy_to_lds((uint4*)smem, (const uint4*)(a.x + (size_t)t0 * H), nt * H / 8);
+    if (a.norm_r) {
+      // the batch's tokens normalised here, one wave each; one block per batch also
+      // stores them for the gate/up launch
+      if (wave < nt)
+        rms_norm_row_wave(a.norm_r + (size_t)(t0 + wave) * H, H, a.eps, lane, (uint16_t*)smem + (size_t)wave * H,
+                          blockIdx.x % a.nRe == 0 ? a.x_w + (size_t)(t0 + wave) * H : nullptr);
+    } else {
+      copy_to_lds((uint4*)smem, (const uint4*)(a.x + (size_t)t0 * H), nt * H / 8);
+    }
     __syncthreads();
     if (e < E) {
       constexpr int RT = NT == 1 ? 1 : kRouteT;  // a lone token computes one chain
@@ -904,8 +935,12 @@ static void launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s
 }
 
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s) {
+                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s,
+                               const uint16_t* norm_r, float eps) {
   LayerArgs a;
+  a.norm_r = norm_r;
+  a.x_w = const_cast<uint16_t*>(x);
+  a.eps = eps;
   a.T = T;
   a.H = L->H;
   a.I = L->I;

@@ -58,8 +58,11 @@ struct LayerDecodeBufs {
   float* o_routed;     // [T*k, H]
   float* o_shared;     // [T, H]
 };
+// norm_r != NULL (chained step): x is a [T, H] buffer that the first launch
+// fills with rms_norm(norm_r) (eps) before the later launches read it.
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
-                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s);
+                               uint16_t* y, const LayerDecodeBufs& b, int32_t* ids_out, float* w_out, hipStream_t s,
+                               const uint16_t* norm_r = nullptr, float eps = 0.f);
 
 size_t mfma_ws_bytes(int E, int H, int I, int total_rows);
 bool mfma_shape_ok(int H, int I);

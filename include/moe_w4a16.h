@@ -219,8 +219,9 @@ int moe_combine(const float* out_perm, const int32_t* pair_pos, const float* top
 /* Normalisation between chained layers: x[t] = bf16(r[t] / sqrt(mean_h
  * r[t, h]^2 + eps)) for r, x bf16 [T, H] (device, 16-byte aligned; x may
  * equal r), H a multiple of 64, eps finite and >= 0.  Squares are summed in
- * fp32 in a fixed order; each element is divided by the fp32 root and
- * rounded once (nearest, ties to even).  The pages chain 47 MoE layers
+ * fp32 in a fixed order; each element is multiplied by the fp32 reciprocal
+ * of the fp32 root and rounded to bf16 (nearest, ties to even), within one
+ * bf16 ulp of the exact quotient.  The pages chain 47 MoE layers
  * ("Recursive Flint: 40B Local Coding Model, Benchmarks", section "What is
  * Recursive Flint?") but do not describe the norms between them: this
  * gain-free RMS normalisation is the stand-in that keeps a chained decode

@@ -566,13 +566,17 @@ def test_chain_teacher_forced(fmt):
     assert prev_ids is not None
 
 
-@pytest.mark.parametrize("fmt,T,NL", [(1, 8, 3), (2, 8, 2), (1, 1, 2)])
-def test_decode_step_matches_calls_and_oracle(fmt, T, NL):
-    """moe_decode_step (one call for NL chained layers) equals the same
-    moe_rms_norm + moe_layer_decode calls bit for bit, and every layer of it,
-    fed the GPU's own residual (teacher forcing), passes the layer checks."""
-    print("decode step", fmt, T, NL, flush=True)
-    H, I, E, k, eps = 2048, 768, 256, 6, 1e-6
+@pytest.mark.parametrize("fmt,T,NL,shape", [(1, 8, 3, "flint"), (2, 8, 2, "flint"), (1, 1, 2, "flint"),
+                                            (1, 16, 2, "flint"), (2, 64, 2, "flint"), (1, 70, 2, "flint"),
+                                            (2, 5, 2, "small"), (3, 16, 2, "flint")])
+def test_decode_step_matches_calls_and_oracle(fmt, T, NL, shape):
+    """moe_decode_step (one call for NL chained layers; each layer's first
+    launch normalises its tokens itself, above 64 tokens the norm kernel
+    does) equals the same moe_rms_norm + moe_layer_decode calls bit for bit,
+    and every layer of it, fed the GPU's own residual (teacher forcing),
+    passes the layer checks."""
+    print("decode step", fmt, T, NL, shape, flush=True)
+    H, I, E, k, eps = (2048, 768, 256, 6, 1e-6) if shape == "flint" else (256, 192, 16, 4, 1e-5)
     layers = [synth.make_layer(fmt, H, I, E, k, synth.seed_of(40, l), DEV) for l in range(NL)]
     ll = moe.LayerList(layers)
     r0 = synth.make_tokens(T, H, 41, DEV)
@@ -601,7 +605,7 @@ def test_decode_step_matches_calls_and_oracle(fmt, T, NL):
     # teacher forcing: layer l on the GPU's r_l
     r = r0
     for l in range(NL):
-        check_layer(layers[l], xs[l], r, r_all[l], ids[l], w[l])
+        check_layer(layers[l], xs[l], r, r_all[l], ids[l], w[l], tokens=None if T <= 16 else [0, T // 3, T - 1])
         r = r_all[l]
     # a step without r_all gives the same result
     nws2 = moe.moe_decode_step_workspace_size(ll, T)

@@ -67,10 +67,20 @@ MOE_DEV moe_bf16x2 e2m1x2_to_bf16(uint32_t word) {
 }
 
 // INT4: nibbles S and S+4 of `word` -> bf16 pair (128 + q_S, 128 + q_{S+4}), exact.
+// magic: 0x43004300 (the bf16 pair (128, 128)) held in a VGPR (int4_magic()):
+// with both constants literal the compiler emits an AND and an OR (CDNA's
+// three-operand encoding takes no literal), with the magic in a register a
+// single v_and_or_b32.
 template <int S>
-MOE_DEV moe_bf16x2 int4x2_to_bf16_off128(uint32_t word) {
-  uint32_t v = ((word >> (4 * S)) & 0x000F000Fu) | 0x43004300u;
+MOE_DEV moe_bf16x2 int4x2_to_bf16_off128(uint32_t word, uint32_t magic) {
+  uint32_t v = ((word >> (4 * S)) & 0x000F000Fu) | magic;
   return __builtin_bit_cast(moe_bf16x2, v);
+}
+
+MOE_DEV uint32_t int4_magic() {
+  uint32_t m = 0x43004300u;
+  asm("" : "+v"(m));
+  return m;
 }
 
 MOE_DEV float dot2_bf16(moe_bf16x2 a, uint32_t b_bits, float c) {

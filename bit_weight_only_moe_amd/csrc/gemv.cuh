@@ -184,14 +184,15 @@ MOE_DEV void piece_dot(const RawPiece& r, int p, const uint16_t* __restrict__ xs
       b1 = 0.f;
       zc = 128.0f + (float)rz;
     }
-    q[0] = int4x2_to_bf16_off128<0>(c.x); q[1] = int4x2_to_bf16_off128<1>(c.x);
-    q[2] = int4x2_to_bf16_off128<2>(c.x); q[3] = int4x2_to_bf16_off128<3>(c.x);
-    q[4] = int4x2_to_bf16_off128<0>(c.y); q[5] = int4x2_to_bf16_off128<1>(c.y);
-    q[6] = int4x2_to_bf16_off128<2>(c.y); q[7] = int4x2_to_bf16_off128<3>(c.y);
-    q[8] = int4x2_to_bf16_off128<0>(c.z); q[9] = int4x2_to_bf16_off128<1>(c.z);
-    q[10] = int4x2_to_bf16_off128<2>(c.z); q[11] = int4x2_to_bf16_off128<3>(c.z);
-    q[12] = int4x2_to_bf16_off128<0>(c.w); q[13] = int4x2_to_bf16_off128<1>(c.w);
-    q[14] = int4x2_to_bf16_off128<2>(c.w); q[15] = int4x2_to_bf16_off128<3>(c.w);
+    const uint32_t mg = int4_magic();
+    q[0] = int4x2_to_bf16_off128<0>(c.x, mg); q[1] = int4x2_to_bf16_off128<1>(c.x, mg);
+    q[2] = int4x2_to_bf16_off128<2>(c.x, mg); q[3] = int4x2_to_bf16_off128<3>(c.x, mg);
+    q[4] = int4x2_to_bf16_off128<0>(c.y, mg); q[5] = int4x2_to_bf16_off128<1>(c.y, mg);
+    q[6] = int4x2_to_bf16_off128<2>(c.y, mg); q[7] = int4x2_to_bf16_off128<3>(c.y, mg);
+    q[8] = int4x2_to_bf16_off128<0>(c.z, mg); q[9] = int4x2_to_bf16_off128<1>(c.z, mg);
+    q[10] = int4x2_to_bf16_off128<2>(c.z, mg); q[11] = int4x2_to_bf16_off128<3>(c.z, mg);
+    q[12] = int4x2_to_bf16_off128<0>(c.w, mg); q[13] = int4x2_to_bf16_off128<1>(c.w, mg);
+    q[14] = int4x2_to_bf16_off128<2>(c.w, mg); q[15] = int4x2_to_bf16_off128<3>(c.w, mg);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {

@@ -49,6 +49,7 @@ constexpr int kLprTokens = 16;
 constexpr int kLprDownTokens = 4;  // the same for down rows (I = 768: 2% faster at 64 tokens than 8)
 constexpr int kMaxPcG = 4;   // gate/up weight pieces per lane held in registers, per matrix
 constexpr int kMaxPcD = 8;   // down weight pieces per lane held in registers
+constexpr int kSepCombineT = 16;  // above this many tokens the combine is a launch of its own
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
@@ -107,6 +108,7 @@ struct LayerArgs {
   int down_stage_bytes;      // launch 3: LDS bytes of the token staging (16-byte multiple)
   int rows_t1;               // one token: output rows per down block, every unit (0: not used)
   int sync_slices;           // slice tickets in the workspace (cleared by launch 1)
+  int sep_combine;           // launch 3 only projects; a fourth launch (k_combine) combines
 };
 
 
@@ -561,9 +563,11 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   int32_t* s_pp = (int32_t*)(s_w + n);                // [n]
   if (routed && tid < kRec) s_rec[tid] = a.rec[(size_t)unit * kRec + tid];
   if (tid == 255) s_nact = a.n_active[0];
-  for (int p = tid; p < n; p += 256) {
-    s_w[p] = a.w[p];
-    s_pp[p] = a.pair_pos[p];
+  if (!a.sep_combine) {
+    for (int p = tid; p < n; p += 256) {
+      s_w[p] = a.w[p];
+      s_pp[p] = a.pair_pos[p];
+    }
   }
   __syncthreads();
   const int n0 = slice * a.rd, n1 = min(H, n0 + a.rd);
@@ -571,13 +575,13 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
     const int e = s_rec[0];
     if (e < 0) return;
     down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed,
-                                             a.o_routed, a.lpr_i, true,
-                       smem);
+                                             a.o_routed, a.lpr_i, !a.sep_combine, smem);
   } else {
     const int r0 = unit * NT;
     down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared,
-                                             a.lpr_is, true, smem);
+                                             a.lpr_is, !a.sep_combine, smem);
   }
+  if (a.sep_combine) return;  // the combine launch reads the outputs after this launch
   block_stores_done();
   const int units = s_nact + a.nsb;
   int* ctr = a.sync + kTicketSlice + 16 * slice;
@@ -917,6 +921,9 @@ static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) 
   }
   hipLaunchKernelGGL((k_layer_down_combine<FMT, NT, GP, IP>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256),
                      lds.down, s, a);
+  if (a.sep_combine)
+    launch_combine(a.o_routed, a.pair_pos, a.w, a.nsb > 0 ? a.o_shared : nullptr, a.residual, a.T, a.k, a.H, a.y,
+                   nullptr, s);
 }
 
 // The Flint shape (hidden 2048, inter 768, the shared expert as wide as the
@@ -997,6 +1004,9 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.down_stage_bytes = (int)align16(stage_bytes(NT, std::max(a.I, a.Is)));
   a.rows_t1 = down_t1_rows(T, a.I, a.Is, a.k, L->shared != nullptr, pw);
   a.sync_slices = (a.H + kRDMin - 1) / kRDMin;
+  // many tokens: the last down block of each slice would combine T x 64 outputs at the
+  // launch's end (a serial tail); a combine launch of its own spreads that over the chip
+  a.sep_combine = T > kSepCombineT;
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const int fmt = L->experts.gate.fmt;
   auto by_fmt = [&](auto nt) {

@@ -337,11 +337,11 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   const int n = T * k;
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   int32_t* hist = (int32_t*)ws;
-  hipLaunchKernelGGL(k_perm_hist, dim3(nchunks), dim3(kPermChunk), E * sizeof(int32_t), s, ids, n, E, hist);
-  hipLaunchKernelGGL(k_perm_scan, dim3((E + 63) / 64), dim3(256), 0, s, nchunks, E, hist, counts);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, counts, hist, offsets,
+  MOE_LAUNCH(k_perm_hist, dim3(nchunks), dim3(kPermChunk), E * sizeof(int32_t), s, ids, n, E, hist);
+  MOE_LAUNCH(k_perm_scan, dim3((E + 63) / 64), dim3(256), 0, s, nchunks, E, hist, counts);
+  MOE_LAUNCH(k_perm_scatter, dim3(nchunks), dim3(kPermChunk), 0, s, ids, n, E, counts, hist, offsets,
                      sorted_pairs, pair_pos);
-  if (x && x_perm) hipLaunchKernelGGL(k_gather_rows, dim3(n), dim3(256), 0, s, x, sorted_pairs, k, H, x_perm);
+  if (x && x_perm) MOE_LAUNCH(k_gather_rows, dim3(n), dim3(256), 0, s, x, sorted_pairs, k, H, x_perm);
   return hipGetLastError();
 }
 

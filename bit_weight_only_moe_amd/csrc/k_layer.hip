@@ -878,17 +878,17 @@ hipError_t launch_grouped_gemv(const moe_ffn_weights* w, const int32_t* active, 
   const size_t lds = std::max((size_t)NT * H * 2 + (size_t)NT * (H / 32) * 4,
                               (size_t)NT * I * 2 + (size_t)NT * (I / 32) * 4);
   if (w->gate.fmt == kFmtNvfp4) {
-    hipLaunchKernelGGL((k_grouped_gateup<kFmtNvfp4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
-    hipLaunchKernelGGL((k_grouped_down<kFmtNvfp4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_gateup<kFmtNvfp4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_down<kFmtNvfp4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   } else if (w->gate.fmt == kFmtInt4Sb) {
-    hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4Sb, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
-    hipLaunchKernelGGL((k_grouped_down<kFmtInt4Sb, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_gateup<kFmtInt4Sb, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_down<kFmtInt4Sb, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   } else if (w->gate.fmt == kFmtBf16) {
-    hipLaunchKernelGGL((k_grouped_gateup<kFmtBf16, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
-    hipLaunchKernelGGL((k_grouped_down<kFmtBf16, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_gateup<kFmtBf16, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_down<kFmtBf16, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   } else {
-    hipLaunchKernelGGL((k_grouped_gateup<kFmtInt4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
-    hipLaunchKernelGGL((k_grouped_down<kFmtInt4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_gateup<kFmtInt4, NT>), dim3(max_active * g.slices_r), dim3(256), lds, s, g);
+    MOE_LAUNCH((k_grouped_down<kFmtInt4, NT>), dim3(max_active * g.slices_d), dim3(256), lds, s, g);
   }
   return hipGetLastError();
 }
@@ -908,22 +908,20 @@ static int down_t1_rows(int T, int I, int Is, int k, bool shared, int pw) {
 }
 
 template <int FMT, int NT, int GP, int IP>
-static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_layer_route_shared<FMT, NT, GP, IP>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s,
-                     a);
-  hipLaunchKernelGGL((k_layer_gateup<FMT, NT, GP, IP>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
+static hipError_t launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
+  MOE_LAUNCH((k_layer_route_shared<FMT, NT, GP, IP>), dim3(a.nR + a.ss_r * a.nsb), dim3(256), lds.route, s, a);
+  MOE_LAUNCH((k_layer_gateup<FMT, NT, GP, IP>), dim3(a.max_active * a.slices_r), dim3(256), lds.gateup, s, a);
   if (NT == 1 && a.rows_t1 > 0) {
     const int units = a.k + (a.nsb > 0 ? 1 : 0);
     const size_t l1 = (size_t)units * a.I * 2 + (size_t)units * (a.I / 32) * 4;
-    hipLaunchKernelGGL((k_layer_down_t1<FMT, IP>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s,
-                       a);
-    return;
+    MOE_LAUNCH((k_layer_down_t1<FMT, IP>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s, a);
+    return hipSuccess;
   }
-  hipLaunchKernelGGL((k_layer_down_combine<FMT, NT, GP, IP>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256),
-                     lds.down, s, a);
-  if (a.sep_combine)
-    launch_combine(a.o_routed, a.pair_pos, a.w, a.nsb > 0 ? a.o_shared : nullptr, a.residual, a.T, a.k, a.H, a.y,
-                   nullptr, s);
+  MOE_LAUNCH((k_layer_down_combine<FMT, NT, GP, IP>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256),
+             lds.down, s, a);
+  if (!a.sep_combine) return hipSuccess;
+  return launch_combine(a.o_routed, a.pair_pos, a.w, a.nsb > 0 ? a.o_shared : nullptr, a.residual, a.T, a.k, a.H,
+                        a.y, nullptr, s);
 }
 
 // The Flint shape (hidden 2048, inter 768, the shared expert as wide as the
@@ -934,11 +932,10 @@ static void launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) 
 // (78 registers at its 128-register bound) and its down needs 180
 // registers, 2.6x slower; one INT4 token gains (24.3 -> 21.4 us).
 template <int FMT, int NT>
-static void launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
+static hipError_t launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
   if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && FMT != kFmtBf16 && (FMT == kFmtNvfp4 || NT == 1))
-    launch_all<FMT, NT, 64, 24>(a, lds, s);
-  else
-    launch_all<FMT, NT, 0, 0>(a, lds, s);
+    return launch_all<FMT, NT, 64, 24>(a, lds, s);
+  return launch_all<FMT, NT, 0, 0>(a, lds, s);
 }
 
 hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
@@ -1009,17 +1006,16 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   a.sep_combine = T > kSepCombineT;
   const DecodeLds lds = decode_lds(T, a.H, a.I, a.Is, a.E, a.k);
   const int fmt = L->experts.gate.fmt;
-  auto by_fmt = [&](auto nt) {
+  auto by_fmt = [&](auto nt) -> hipError_t {
     constexpr int N = decltype(nt)::value;
-    if (fmt == kFmtNvfp4) launch_shape<kFmtNvfp4, N>(a, lds, s);
-    else if (fmt == kFmtInt4Sb) launch_shape<kFmtInt4Sb, N>(a, lds, s);
-    else if (fmt == kFmtBf16) launch_shape<kFmtBf16, N>(a, lds, s);
-    else launch_shape<kFmtInt4, N>(a, lds, s);
+    if (fmt == kFmtNvfp4) return launch_shape<kFmtNvfp4, N>(a, lds, s);
+    if (fmt == kFmtInt4Sb) return launch_shape<kFmtInt4Sb, N>(a, lds, s);
+    if (fmt == kFmtBf16) return launch_shape<kFmtBf16, N>(a, lds, s);
+    return launch_shape<kFmtInt4, N>(a, lds, s);
   };
-  if (NT == 1) by_fmt(std::integral_constant<int, 1>{});
-  else if (NT == 2) by_fmt(std::integral_constant<int, 2>{});
-  else by_fmt(std::integral_constant<int, 4>{});
-  return hipGetLastError();
+  if (NT == 1) return by_fmt(std::integral_constant<int, 1>{});
+  if (NT == 2) return by_fmt(std::integral_constant<int, 2>{});
+  return by_fmt(std::integral_constant<int, 4>{});
 }
 
 }  // namespace moe

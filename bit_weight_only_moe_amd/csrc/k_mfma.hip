@@ -924,23 +924,23 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   g.out = out;
   // 64-row tiles everywhere (k_mfma_bl / k_mfma_bd).
   if (split && bd_k_ok(w->gate.fmt, H) && bd_k_ok(w->gate.fmt, I)) {
-    hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, 64, 0, big, small);
+    MOE_LAUNCH(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, 64, 0, big, small);
     const unsigned b8 = (unsigned)((max_big + 7) / 8 * 8);
     MfmaArgs ga = g;
     ga.tiles = big;
     ga.tile_rows = 64;
     if (w->gate.fmt == kFmtNvfp4) {
-      hipLaunchKernelGGL((k_mfma_bl<kFmtNvfp4, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
-      hipLaunchKernelGGL((k_mfma_bl<kFmtNvfp4, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
+      MOE_LAUNCH((k_mfma_bl<kFmtNvfp4, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
+      MOE_LAUNCH((k_mfma_bl<kFmtNvfp4, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
     } else {
-      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
-      hipLaunchKernelGGL((k_mfma_bd<kFmtInt4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
+      MOE_LAUNCH((k_mfma_bd<kFmtInt4, 2, true>), dim3(b8 * (I / 128)), dim3(256), 0, s, ga);
+      MOE_LAUNCH((k_mfma_bd<kFmtInt4, 2, false>), dim3(b8 * (H / 256)), dim3(256), 0, s, ga);
     }
     return hipGetLastError();
   }
   // Otherwise LDS-staged weights: 128-row tiles, with a final remainder of at
   // most 64 rows in a 64-row tile when the shapes allow.
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, kBM, split ? 1 : 0, big, small);
+  MOE_LAUNCH(k_tile_table, dim3(1), dim3(1024), 0, s, offsets, E, total_rows, kBM, split ? 1 : 0, big, small);
   // one block per (row tile, column slice); tiles rounded up to a multiple of the 8 XCDs
   const unsigned big8 = (unsigned)((max_big + 7) / 8 * 8), small8 = (unsigned)((E + 7) / 8 * 8);
   MfmaArgs gb = g, gs = g;
@@ -950,15 +950,15 @@ hipError_t launch_grouped_mfma(const moe_ffn_weights* w, int E, const int32_t* o
   gs.tile_rows = 64;
   const dim3 gu_small(small8 * (I / 128)), dn_small(small8 * (H / 256));
   if (w->gate.fmt == kFmtNvfp4) {
-    hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtNvfp4, 1>), gu_small, dim3(256), 0, s, gs);
-    hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtNvfp4, 1>), dn_small, dim3(256), 0, s, gs);
+    MOE_LAUNCH((k_mfma_gateup<kFmtNvfp4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
+    if (split) MOE_LAUNCH((k_mfma_gateup<kFmtNvfp4, 1>), gu_small, dim3(256), 0, s, gs);
+    MOE_LAUNCH((k_mfma_down<kFmtNvfp4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
+    if (split) MOE_LAUNCH((k_mfma_down<kFmtNvfp4, 1>), dn_small, dim3(256), 0, s, gs);
   } else {
-    hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_gateup<kFmtInt4, 1>), gu_small, dim3(256), 0, s, gs);
-    hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
-    if (split) hipLaunchKernelGGL((k_mfma_down<kFmtInt4, 1>), dn_small, dim3(256), 0, s, gs);
+    MOE_LAUNCH((k_mfma_gateup<kFmtInt4, 2>), dim3(big8 * (I / 64)), dim3(256), 0, s, gb);
+    if (split) MOE_LAUNCH((k_mfma_gateup<kFmtInt4, 1>), gu_small, dim3(256), 0, s, gs);
+    MOE_LAUNCH((k_mfma_down<kFmtInt4, 2>), dim3(big8 * (H / 128)), dim3(256), 0, s, gb);
+    if (split) MOE_LAUNCH((k_mfma_down<kFmtInt4, 1>), dn_small, dim3(256), 0, s, gs);
   }
   return hipGetLastError();
 }

@@ -45,6 +45,16 @@ int layer_decode_sync_words(int H);
 size_t layer_decode_rec_ints(int T, int E, int k);
 
 // Workspace buffers of the three-launch decode layer.
+// Launch a kernel and return from the enclosing function with its launch
+// status if that failed (taken at once, before a later launch or status
+// query can replace or clear it).
+#define MOE_LAUNCH(...)                       \
+  do {                                        \
+    hipLaunchKernelGGL(__VA_ARGS__);          \
+    const hipError_t moe_e_ = hipGetLastError(); \
+    if (moe_e_ != hipSuccess) return moe_e_;  \
+  } while (0)
+
 struct LayerDecodeBufs {
   int* sync;           // ticket counters, zero before the first call, left zero
   float* logits;       // [T, E]

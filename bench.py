@@ -425,14 +425,15 @@ def dense_entry(c, fmt_name, T, K, W, cpu_seconds, rows=150144):
 
     ms = c.timed(step, K, W)
     ms_step = ms / K
-    gbs = mb * ((T + 7) // 8) / (ms_step * 1e-3) / 1e9
+    gbs = mb * ((T + 63) // 64) / (ms_step * 1e-3) / 1e9  # algorithmic: the matrix once per 64 tokens
     entry = {"workload": "dense_w4a16_gemv output head %d x 2048 T=%d %s" % (rows, T, fmt_name),
              "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": K, "warmup": W,
              "weight_copies": R, "matrix_bytes": mb,
              "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get(("dense_head_T%d" % T, fmt_name)),
-                          "kernel": "k_dense_gemv (one call), events on the launch stream",
-                          "bytes": "the packed matrix once per batch of up to 8 tokens"},
+                          "kernel": "%s (one call), events on the launch stream"
+                                    % ("k_mfma_bl dense form" if (T >= 8 and fmt == 1) else "k_dense_gemv"),
+                          "bytes": "the packed matrix once per 64 tokens"},
              "cpu_baseline": None}
     if cpu_seconds > 0:
         import oracle

@@ -18,6 +18,10 @@ namespace moe {
 constexpr int kDenseNT = 8;       // tokens staged per launch (8 rows of up to 3840 in 64 KB of LDS)
 constexpr int kDenseLpr = 16;     // lanes per row
 constexpr int kDenseMaxPcl = 8;   // pieces per lane held in registers
+// From this many tokens NVFP4 runs on the matrix cores.  Head (150,144 x 2048), same box:
+// vector units 38 / 50 / 82 / 160 us at 2 / 4 / 8 / 16 tokens, matrix cores 67 us at all four
+// (587 blocks of 256 columns, two per CU: a second partial wave of blocks).
+constexpr int kDenseMfmaMinT = 8;
 
 struct DenseArgs {
   MatDev m;
@@ -145,6 +149,10 @@ int dense_max_tokens() { return kDenseNT; }
 hipError_t launch_dense_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
                              hipStream_t s) {
   if (m->fmt == kFmtBf16) return hipErrorInvalidValue;  // 4-bit formats only
+  // several NVFP4 tokens: the matrix cores (the vector units would issue T dot products per
+  // weight; the matrix once per 64 tokens instead of once per 8)
+  if (T >= kDenseMfmaMinT && m->fmt == kFmtNvfp4 && m->cols % 256 == 0 && m->cols <= 2048)
+    return launch_dense_mfma(m, expert, x, T, out, s);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;

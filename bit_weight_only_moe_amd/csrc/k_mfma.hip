@@ -53,6 +53,7 @@ struct MfmaArgs {
   const float *gts, *uts, *dts; // NVFP4 tensor scales
   uint16_t* h;                  // [rows, I]
   float* out;                   // [rows, H]
+  int ldo;                      // dense form: row stride of out
 };
 
 MOE_DEV bool tile_of(const MfmaArgs& g, int mt, int& e, int& r0, int& r1) {
@@ -584,18 +585,32 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bd(MfmaArgs g) {
 // consecutive lanes, so one load instruction covers 8 whole cache lines
 // rather than 16-byte pieces of 32 (measured: 2-4% faster than per-lane
 // streaming into registers).  LDS: activations 2 x 8 KB, codes 2 x 32 KB.
-template <int FMT, bool GU>
+// DENSE (down form only): one matrix and one tile of g.rows <= 64 rows (no
+// tile table); block b takes output columns [256 b, 256 b + 256) of N, the
+// last slice partial (weight rows clamped to N - 1, their outputs not
+// stored); outputs at row stride g.ldo.
+template <int FMT, bool GU, bool DENSE = false>
 __global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
   static_assert(FMT == kFmtNvfp4, "NVFP4 only");
+  static_assert(!(DENSE && GU), "the dense form is a plain product");
   constexpr int RF = 2, BM = 64, D = 4, NB = GU ? 128 : 256, AV = 2;
   __shared__ uint4 As[2][BM * 8];
   __shared__ uint4 Bs[2][256 * 8];  // [256 weight rows][128 bytes], chunk c at c ^ (row & 7)
   const int K = GU ? g.H : g.I, N = GU ? g.I : g.H;
   int tile, slice;
-  block_tile_chunked(N / NB, g.tiles[0], tile, slice);
   int e, r0, r1;
-  if (!tile_of(g, tile, e, r0, r1)) return;
+  if (DENSE) {
+    slice = blockIdx.x;
+    e = 0;
+    r0 = 0;
+    r1 = g.rows;
+  } else {
+    block_tile_chunked(N / NB, g.tiles[0], tile, slice);
+    if (!tile_of(g, tile, e, r0, r1)) return;
+  }
   const int n0 = slice * NB;
+  // weight row n of this block, clamped into the matrix (dense: the last slice is partial)
+  auto wrow = [&](int n) __attribute__((always_inline)) { return DENSE ? min(n, N - 1) : n; };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int a_chunk = tid & 7;
   const u32x4_t* asrc[AV];
@@ -613,7 +628,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
   // down: output column br
   auto brow_codes = [&](int br) __attribute__((always_inline)) {
     if (GU) return (br < 128 ? g.gc : g.uc) + ((size_t)e * N + n0 + (br & 127)) * (K / 2);
-    return g.dc + ((size_t)e * N + n0 + br) * (K / 2);
+    return g.dc + ((size_t)e * N + wrow(n0 + br)) * (K / 2);
   };
   // this thread's 8 group loads: rows i*32 + tid/8, 16-byte chunk tid % 8
   const uint8_t* gsrc[8];
@@ -625,7 +640,7 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
 #pragma unroll
   for (int cf = 0; cf < 2; ++cf) {
     lrow[cf] = GU ? cf * 128 + wave * 32 + l32 : wave * 64 + cf * 32 + l32;
-    const size_t row = GU ? (size_t)e * N + n0 + wave * 32 + l32 : (size_t)e * N + n0 + lrow[cf];
+    const size_t row = GU ? (size_t)e * N + n0 + wave * 32 + l32 : (size_t)e * N + wrow(n0 + lrow[cf]);
     bsp[cf] = (GU ? (cf ? g.us : g.gs) : g.ds) + row * (K / 16);
   }
   u32x4_t ar[AV][D];
@@ -721,11 +736,38 @@ __global__ void __launch_bounds__(256, 2) k_mfma_bl(MfmaArgs g) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = rf * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          if (r0 + row < r1) g.out[(size_t)(r0 + row) * N + col] = acc[cf][rf][i] * ts;
+          if (r0 + row < r1 && (!DENSE || col < N))
+            g.out[(size_t)(r0 + row) * (DENSE ? g.ldo : N) + col] = acc[cf][rf][i] * ts;
         }
       }
     }
   }
+}
+
+// Dense product out[t, n] = tensor_scale * sum_k x[t, k] W[n, k] for one NVFP4
+// matrix (expert `expert` of the stack) on the matrix cores: tokens in tiles
+// of up to 64 rows, one block per 256 output columns.  Needs K % 256 == 0 and
+// K <= 2048.
+hipError_t launch_dense_mfma(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
+                             hipStream_t s) {
+  if (m->fmt != kFmtNvfp4 || !bd_k_ok(m->fmt, m->cols)) return hipErrorInvalidValue;
+  const size_t rc = (size_t)m->rows * m->cols;
+  MfmaArgs g{};
+  g.H = m->rows;  // N: output columns
+  g.I = m->cols;  // K
+  g.k = 1;
+  g.dc = m->codes + (size_t)expert * (rc / 2);
+  g.ds = (const uint8_t*)m->scales + (size_t)expert * (rc / 16);
+  g.dts = m->tensor_scale + expert;
+  g.ldo = m->rows;
+  const int nblk = (m->rows + 255) / 256;
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    g.rows = std::min(64, T - t0);
+    g.h = const_cast<uint16_t*>(x) + (size_t)t0 * m->cols;
+    g.out = out + (size_t)t0 * m->rows;
+    MOE_LAUNCH((k_mfma_bl<kFmtNvfp4, false, true>), dim3(nblk), dim3(256), 0, s, g);
+  }
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------ router (large batches)

@@ -13,6 +13,9 @@ namespace moe {
 
 // Dense GEMV out[T, rows] = W_expert x (tokens in batches of dense_max_tokens()).
 int dense_max_tokens();
+// The same product on the matrix cores (NVFP4, K % 256 == 0, K <= 2048), any T.
+hipError_t launch_dense_mfma(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
+                             hipStream_t s);
 hipError_t launch_dense_gemv(const moe_w4_matrix* m, int expert, const uint16_t* x, int T, float* out,
                              hipStream_t s);
 hipError_t launch_dequant_expert(int fmt, int rows, int cols, const uint8_t* codes, const void* scales,

@@ -138,7 +138,9 @@ int moe_dequant_w4(const moe_w4_matrix* m, int expert, float* out, void* stream)
  * of 64 up to 3840), x bf16 [T, cols], out fp32 [T, rows] (device,
  * caller-owned, 16-byte aligned); weights exactly dequantised, fp32
  * accumulation, the NVFP4 tensor scale applied last.  Tokens are taken in
- * batches of 8, each batch streaming the matrix once.  Source: the 4-bit
+ * batches of 8, each batch streaming the matrix once; from 8 tokens NVFP4
+ * with cols a multiple of 256 up to 2048 runs on the matrix cores instead
+ * (batches of 64 tokens; the same bound, another summation order).  Source: the 4-bit
  * output head of "Recursive Flint: 40B Local Coding Model, Benchmarks"
  * (section "How Recursive built Flint") over its 150,144-token vocabulary
  * ("What is Recursive Flint?"); the same call serves any dense projection.

@@ -298,9 +298,11 @@ def test_grouped_ffn_gemv(fmt, H, I, E, k, T, seed, scales):
 # ------------------------------------------------------------------ dense GEMV (output head)
 
 DENSE_CASES = [
-    # fmt, rows, cols, T, seed, scales, sampled: the 4-bit head over the 150,144-token vocabulary,
-    # one token, a batch, and 11 tokens (two batches of at most 8); other shapes take the
-    # runtime-shape kernel
+    # fmt, rows, cols, T, seed, scales, sampled: the 4-bit head over the 150,144-token vocabulary
+    # (not a multiple of 256 rows): up to 7 tokens on the vector units, from 8 NVFP4 tokens on
+    # the matrix cores (the last 256-column slice partial), INT4 in two batches of at most 8
+    # tokens; other shapes take the runtime-shape kernel, or the matrix cores (NVFP4, from 8
+    # tokens, cols a multiple of 256 up to 2048)
     (1, 150144, 2048, 1, 70, "narrow", True),
     (1, 150144, 2048, 5, 71, "full", True),
     (2, 150144, 2048, 11, 72, "narrow", True),
@@ -308,6 +310,9 @@ DENSE_CASES = [
     (1, 1000, 3840, 3, 74, "narrow", False),
     (2, 777, 192, 9, 75, "full", False),
     (3, 33, 256, 1, 76, "narrow", False),
+    (1, 100, 256, 9, 77, "full", False),
+    (1, 600, 1024, 70, 78, "narrow", False),
+    (1, 150144, 2048, 8, 79, "narrow", True),
 ]
 
 

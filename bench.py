@@ -59,12 +59,13 @@ WARM_MS = 50.0            # untimed graph replays queued right before the timed 
 # counters read 1 GiB each for a plain 1 GiB device copy (profiles/hbm_traffic_counters.md).
 # Workloads not listed report null.
 TRAFFIC_BYTES = {
-    ("decode_b1", "nvfp4"): 21.49e6,
-    ("decode_T16", "nvfp4"): 221.7e6,
-    ("decode_T64", "nvfp4"): 560.6e6,
+    ("decode_b1", "nvfp4"): 21.53e6,
+    ("decode_T16", "nvfp4"): 221.8e6,
+    ("decode_T64", "nvfp4"): 560.2e6,
     ("chain_b8", "nvfp4"): 5.90e9,
     ("dense_head_T1", "nvfp4"): 173.7e6,
-    ("prefill", "nvfp4"): 1236.8e6,
+    ("dense_head_T8", "nvfp4"): 214.6e6,
+    ("prefill", "nvfp4"): 1236.6e6,
 }
 
 
@@ -150,6 +151,7 @@ class Ctx:
         stream, queued together (with --eager: the K steps launched directly after a flush).
         Returns ms."""
         t, s = self.torch, self.stream
+        t.cuda.synchronize()  # the inputs were made on the default stream; the steps run on s
         with t.cuda.stream(s):
             for i in range(W):
                 body(i, s)

@@ -403,24 +403,17 @@ size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T) {
   return decode_ws(L, T, nullptr, nullptr);
 }
 
-// bf16 expert weights take the layer path for a lone token only: the
-// several-token kernels in this format are switched off after an unexplained
-// memory fault under load (their parity tests pass; no out-of-range access
-// has been found in them).  The grouped FFN call still takes bf16 at any T.
-static int check_bf16_tokens(const moe_layer_weights* L, int T, const char* who) {
-  if (L->experts.gate.fmt == MOE_FMT_BF16 && T > 1)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 expert weights with T=%d > 1 are not supported on the layer path",
-                who, T);
-  return MOE_OK;
-}
+// bf16 expert weights with several tokens take the composed kernels (router,
+// permute, grouped GEMV FFN, combine): the fused several-token kernels in this
+// format are switched off after an unexplained memory fault under load (their
+// parity tests passed; no out-of-range access has been found in them).
+static bool bf16_composed(const moe_layer_weights* L, int T) { return L->experts.gate.fmt == MOE_FMT_BF16 && T > 1; }
 
 static int check_decode_args(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual, int T,
                              const uint16_t* y, const int32_t* ids_out, const float* w_out, const char* who) {
   int rc = check_layer(L, who);
   if (rc) return rc;
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", who, T);
-  rc = check_bf16_tokens(L, T, who);
-  if (rc) return rc;
   if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "%s: null x or y", who);
   if ((ids_out == nullptr) != (w_out == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "%s: ids_out and w_out must both be given or both be NULL", who);
@@ -483,8 +476,6 @@ int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_
   int rc = check_step(layers, n_layers, "moe_decode_step");
   if (rc) return rc;
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: T=%d < 0", T);
-  rc = check_bf16_tokens(&layers[0], T, "moe_decode_step");
-  if (rc) return rc;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: eps must be finite, >= 0");
   if (!r_in || !r_out) return fail(MOE_ERR_INVALID_ARG, "moe_decode_step: null r_in or r_out");
   if ((ids_out == nullptr) != (w_out == nullptr))
@@ -548,7 +539,7 @@ static int layer_decode_on(const moe_layer_weights* L, const uint16_t* x, const 
   hipStream_t s = as_stream(stream);
   const int E = L->E, k = L->k, H = L->H;
   const int Is = L->shared ? L->shared->gate.rows : 0;
-  if (moe::layer_decode_lds(T, H, L->I, Is, E, k) > 0) {
+  if (moe::layer_decode_lds(T, H, L->I, Is, E, k) > 0 && !bf16_composed(L, T)) {
     moe::LayerDecodeBufs b;
     b.sync = d.sync;
     b.logits = d.logits;

@@ -251,9 +251,9 @@ int moe_rms_norm(const uint16_t* r, int T, int H, float eps, uint16_t* x, void* 
  * kernels use to hand work to the last block of a group; every call leaves
  * them reset to zero.  Calls sharing a
  * workspace must not run concurrently.  The shared expert must have the
- * same format and hidden size as the routed experts.  MOE_FMT_BF16 weights:
- * T = 1 only (T > 1 returns MOE_ERR_UNSUPPORTED; moe_grouped_w4a16_ffn takes
- * them at any T). */
+ * same format and hidden size as the routed experts.  MOE_FMT_BF16 weights
+ * with T > 1 take the composed path at every T (the same results as the
+ * separate calls in GEMV mode). */
 size_t moe_layer_decode_workspace_size(const moe_layer_weights* L, int T);
 int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16_t* residual,
                      int T, uint16_t* y, int32_t* ids_out, float* w_out,
@@ -275,8 +275,7 @@ int moe_layer_decode(const moe_layer_weights* L, const uint16_t* x, const uint16
  * moe_decode_step_workspace_size(layers, n_layers, T, r_all != NULL) bytes,
  * 256-byte aligned, zero-filled before its first use (it holds a layer
  * workspace).  The result equals the same sequence of moe_rms_norm and
- * moe_layer_decode calls bit for bit.  MOE_FMT_BF16 weights: T = 1 only, as
- * for moe_layer_decode. */
+ * moe_layer_decode calls bit for bit. */
 size_t moe_decode_step_workspace_size(const moe_layer_weights* layers, int n_layers, int T, int with_r_all);
 int moe_decode_step(const moe_layer_weights* layers, int n_layers, const uint16_t* r_in, int T, float eps,
                     uint16_t* r_out, uint16_t* r_all, int32_t* ids_out, float* w_out, void* ws,

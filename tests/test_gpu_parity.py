@@ -418,9 +418,6 @@ def check_layer(layer, x, residual, y, ids, w, tokens=None, ws=None):
     return err
 
 
-BF16_MULTI_OFF = pytest.mark.skip(reason="bf16 weights with T > 1: layer path switched off (unexplained memory "
-                                          "fault in a timed T=16 run); the call returns MOE_ERR_UNSUPPORTED")
-
 LAYER_CASES = [
     # name, fmt, H, I, E, k, T, seed, residual
     ("tiny_int4_T4", 2, 256, 128, 32, 6, 4, 0, False),
@@ -457,12 +454,12 @@ LAYER_CASES = [
     ("ragged_int4sb_H192_I320_T1", 3, 192, 320, 8, 6, 1, 28, False),
     # BF16 weights
     ("flint_bf16_T1", 4, 2048, 768, 256, 6, 1, 29, True),
-    # several tokens on bf16 weights: the layer call rejects them (the
+    # several tokens on bf16 weights take the composed kernels (the fused
     # several-token kernels in this format are switched off after a memory
     # fault in a timed run whose cause is not found)
-    pytest.param("flint_bf16_T4", 4, 2048, 768, 256, 6, 4, 30, False, marks=BF16_MULTI_OFF),
-    pytest.param("flint_bf16_T16", 4, 2048, 768, 256, 6, 16, 31, True, marks=BF16_MULTI_OFF),
-    pytest.param("tiny_bf16_T64", 4, 256, 128, 32, 6, 64, 32, False, marks=BF16_MULTI_OFF),
+    ("flint_bf16_T4", 4, 2048, 768, 256, 6, 4, 30, False),
+    ("flint_bf16_T16", 4, 2048, 768, 256, 6, 16, 31, True),
+    ("tiny_bf16_T64", 4, 256, 128, 32, 6, 64, 32, False),
     ("ragged_bf16_H192_I320_T1", 4, 192, 320, 8, 6, 1, 33, True),
 ]
 
@@ -573,7 +570,8 @@ def test_chain_teacher_forced(fmt):
 
 @pytest.mark.parametrize("fmt,T,NL,shape", [(1, 8, 3, "flint"), (2, 8, 2, "flint"), (1, 1, 2, "flint"),
                                             (1, 16, 2, "flint"), (2, 64, 2, "flint"), (1, 70, 2, "flint"),
-                                            (2, 5, 2, "small"), (3, 16, 2, "flint")])
+                                            (2, 5, 2, "small"), (3, 16, 2, "flint"), (4, 1, 2, "small"),
+                                            (4, 6, 2, "small")])
 def test_decode_step_matches_calls_and_oracle(fmt, T, NL, shape):
     """moe_decode_step (one call for NL chained layers; each layer's first
     launch normalises its tokens itself, above 64 tokens the norm kernel
@@ -883,8 +881,7 @@ def test_prefill_4096_zipf_sampled():
     assert err <= TOL_LAYER
 
 
-@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100), (3, 100),
-                                   pytest.param(4, 100, marks=BF16_MULTI_OFF)])
+@pytest.mark.parametrize("fmt,T", [(2, 200), (1, 70), (1, 100), (3, 100), (4, 100)])
 def test_layer_decode_large_batch_uses_grouped_gemm(fmt, T):
     """Above 64 tokens the layer is composed from the separate calls; 70 tokens
     (420 pairs, under two per expert) take the GEMV grouped FFN, 100 and 200

@@ -6,8 +6,9 @@ inter 768, NVFP4 W4A16 weights, bf16 activations).  One step = one
 moe_layer_decode call on one token: router GEMV, top-k + softmax, expert
 grouping, gate/up + SwiGLU, down projection, shared expert and combine.
 The same JSON line carries a ``sweep`` object with the rest of the metric:
-decode at 1/4/16/64 tokens in the three weight formats (NVFP4, INT4 with a
-zero point, INT4 with scale and bias), the 47-layer batch-8 chained decode
+decode at 1/4/16/64 tokens in the three 4-bit weight formats (NVFP4, INT4
+with a zero point, INT4 with scale and bias) and in BF16 weights for
+comparison, the 47-layer batch-8 chained decode
 step, and the 4096-token Zipf(1.1) prefill in NVFP4 and zero-point INT4,
 each with its roofline fraction and a short timing of the float64 CPU
 oracle on a bounded sample of the same workload.
@@ -226,7 +227,10 @@ def decode_entry(c, fmt_name, T, K, W, cpu_seconds):
                           "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC_BYTES.get((wl, fmt_name)),
                           "kernel": "moe_layer_decode (one layer call: %s), events on the launch stream"
                                     % ("k_layer_route_shared + k_layer_gateup + k_layer_down_t1" if T == 1 else
-                                       "k_layer_route_shared + k_layer_gateup + k_layer_down_combine"),
+                                       "the composed kernels: router, top-k, permute, grouped GEMV gate/up and "
+                                       "down for the routed and shared experts, k_combine" if fmt_name == "bf16" else
+                                       "k_layer_route_shared + k_layer_gateup + k_layer_down_combine"
+                                       + (" + k_combine" if T > 16 else "")),
                           "bytes": "expert weights of the distinct touched experts + shared expert, per call"},
              "cpu_baseline": None}
     if cpu_seconds > 0:
@@ -491,7 +495,8 @@ def line_from(entry, fmt_name, value_key, unit, K, W):
     cfg = {k: v for k, v in entry.items() if k not in ("roofline", "cpu_baseline", "ms_per_step", "steps", "warmup")}
     return {"metric": METRIC, "value": entry[value_key], "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
             "ms_per_step": entry["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "w4(%s)/bf16 act/fp32 acc" % fmt_name, "data": "synthetic", "config": cfg,
+            "dtype": "%s/bf16 act/fp32 acc" % ("w16(bf16)" if fmt_name == "bf16" else "w4(%s)" % fmt_name),
+            "data": "synthetic", "config": cfg,
             "roofline": entry["roofline"], "cpu_baseline": entry["cpu_baseline"]}
 
 
@@ -535,7 +540,7 @@ def main():
     head = decode_entry(c, "nvfp4", 1, K, W, cpu)
     sweep = {}
     t_start = time.perf_counter()
-    for fmt_name in ("nvfp4", "int4", "int4sb"):
+    for fmt_name in ("nvfp4", "int4", "int4sb", "bf16"):
         for T in (1, 4, 16, 64):
             if fmt_name == "nvfp4" and T == 1:
                 continue
@@ -546,7 +551,7 @@ def main():
             sweep["chain_b8_nvfp4"] = chain_entry(c, "nvfp4", Kc, Wc, scpu)
             print("[bench] chain done (%.0f s)" % (time.perf_counter() - t_start), file=sys.stderr, flush=True)
         c.drop(fmt_name)
-        if fmt_name == "int4sb":
+        if fmt_name in ("int4sb", "bf16"):
             continue       # the matrix-core grouped GEMM takes NVFP4 and zero-point INT4 only
         sweep["prefill_%s" % fmt_name] = prefill_entry(c, fmt_name, Kc, Wc, scpu)
         c.torch.cuda.empty_cache()

@@ -27,7 +27,8 @@
  *   - Tensor arguments are DEVICE pointers owned by the caller, except the
  *     weight descriptor structs themselves, which live in host memory (their
  *     members point to device memory).  The library allocates and frees
- *     nothing and keeps no device state between calls.
+ *     nothing and keeps no device state between calls, except the static
+ *     scratch array of moe_layer_decode_noalloc (see there).
  *   - bf16 and fp16 values are passed as uint16_t bit patterns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; they never synchronise and never read device
@@ -91,9 +92,9 @@ enum {
 enum { MOE_FMT_NVFP4 = 1, MOE_FMT_INT4_G64 = 2, MOE_FMT_INT4_SB = 3, MOE_FMT_BF16 = 4 };
 enum { MOE_MODE_AUTO = 0, MOE_MODE_GEMV = 1, MOE_MODE_MFMA = 2 };
 
-/* One packed 4-bit matrix stack (host struct, device pointers). */
+/* One weight matrix stack: packed 4-bit, or BF16 (host struct, device pointers). */
 typedef struct moe_w4_matrix {
-  int fmt;                   /* MOE_FMT_NVFP4, MOE_FMT_INT4_G64 or MOE_FMT_INT4_SB */
+  int fmt;                   /* MOE_FMT_NVFP4, MOE_FMT_INT4_G64, MOE_FMT_INT4_SB or MOE_FMT_BF16 */
   int num_experts;           /* E of this stack */
   int rows, cols;            /* out, in (cols = reduction axis); cols <= 3840 (the GEMV
                                 kernels stage 8 tokens' rows of cols in 64 KB of LDS) */

@@ -37,7 +37,9 @@ def without_workspace(L, x, res, T, k):
     return y, ids, w
 
 
-@pytest.mark.parametrize("fmt,sizes", [(1, (16, 4)), (2, (8, 1)), (1, (64, 1, 5))])
+# bf16 weights: several tokens take the composed kernels, one token the fused ones, both on
+# the same static array
+@pytest.mark.parametrize("fmt,sizes", [(1, (16, 4)), (2, (8, 1)), (1, (64, 1, 5)), (4, (16, 1))])
 def test_noalloc_matches_workspace_path(fmt, sizes):
     """Consecutive calls on the shared static array, each smaller than the one
     before and differently routed, equal moe_layer_decode on a fresh workspace

@@ -55,6 +55,13 @@ constexpr bool fmt_shared_early(int fmt) { return fmt == kFmtNvfp4; }
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
+// Down blocks of the looping down kernel: about four blocks per CU, each taking
+// several units of its slice (measured against one unit per block, the 8-token
+// 47-layer chain 2238 -> 2148 us, 16 tokens 66.4 -> 63.9 us; at 64 tokens and in
+// the runtime-shape kernels the loop's extra registers cost more than it saves).
+constexpr int kDownBlocks = 1024;
+constexpr int kMaxDownUnits = 8;
+constexpr bool down_loops(int fmt, int nt, int ip) { return fmt == kFmtNvfp4 && nt == 2 && ip > 0; }
 
 // Compile-time shapes: GP = H / 32 and IP = I / 32 pieces per gate/up and down
 // row (0: the runtime shape).  Lanes per row as the launcher picks them at
@@ -111,6 +118,7 @@ struct LayerArgs {
   int rows_t1;               // one token: output rows per down block, every unit (0: not used)
   int sync_slices;           // slice tickets in the workspace (cleared by launch 1)
   int sep_combine;           // launch 3 only projects; a fourth launch (k_combine) combines
+  int down_groups;           // launch 3: unit groups per slice (block g takes units g, g + G, ...)
   int shared_in_gateup;      // the shared expert's gate/up runs in launch 2 instead of launch 1
 };
 
@@ -354,13 +362,20 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
     }
     __syncthreads();
     if (e < E) {
-      constexpr int RT = NT == 1 ? 1 : kRouteT;  // a lone token computes one chain
-      float acc[RT];
-      router_dots<RT>(a.w_router + (size_t)e * H, (const uint16_t*)smem, H, nt, lane, acc, wv);
       // device-coherent stores: the block that takes the batch's last ticket reads them
+      auto dots = [&](auto rt) __attribute__((always_inline)) {
+        constexpr int RT = decltype(rt)::value;
+        float acc[RT];
+        router_dots<RT>(a.w_router + (size_t)e * H, (const uint16_t*)smem, H, nt, lane, acc, wv);
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        if (t < nt && lane == 63) st_dev(a.logits + (size_t)(t0 + t) * E + e, acc[t]);
+        for (int t = 0; t < RT; ++t)
+          if (t < nt && lane == 63) st_dev(a.logits + (size_t)(t0 + t) * E + e, acc[t]);
+      };
+      // a lone token (or batches of one token) computes one chain
+      if (NT == 1 || a.rt == 1)
+        dots(std::integral_constant<int, 1>{});
+      else
+        dots(std::integral_constant<int, kRouteT>{});
     }
   }
   block_stores_done();  // every logit this block stored is visible chip-wide
@@ -560,20 +575,28 @@ __global__ void __launch_bounds__(256, FMT != kFmtNvfp4 && NT > 1 ? 4 : 1) k_lay
 template <int FMT, int NT, int GP, int IP>
 __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_rec[kRec];
+  __shared__ int s_rec[kMaxDownUnits][3];
   __shared__ int ticket, s_nact;
   const int tid = threadIdx.x;
   const int T = a.T, H = a.H, k = a.k, n = T * k;
-  // the shared expert's units come first: they carry NT tokens each and
-  // would otherwise be the launch's tail
-  const int slice = blockIdx.x % a.slices_d, u = blockIdx.x / a.slices_d;
-  const bool routed = u >= a.nsb;
-  const int unit = routed ? u - a.nsb : u;
+  // Block (group g, slice) takes units g, g + G, g + 2G, ... of its slice
+  // (G = down_groups; one unit per block, G = every unit, except in the
+  // compiled-shape NVFP4 kernel for 2 to 16 tokens: the others would need more
+  // registers for the loop).  The shared expert's units come first: they
+  // carry NT tokens each and would otherwise be the launch's tail.
+  constexpr bool LOOP = down_loops(FMT, NT, IP);
+  const int max_units = a.nsb + a.max_active;
+  const int slice = blockIdx.x % a.slices_d, g = blockIdx.x / a.slices_d, G = LOOP ? a.down_groups : max_units;
+  const int nmine = g < max_units ? (LOOP ? (max_units - 1 - g) / G + 1 : 1) : 0;  // <= kMaxDownUnits
   // the combine's weights and pair positions (written by launch 1), loaded
-  // with the record so the last block needs one more round trip only
+  // with the records so the last block needs one more round trip only
   float* s_w = (float*)(smem + a.down_stage_bytes);  // [n]
   int32_t* s_pp = (int32_t*)(s_w + n);                // [n]
-  if (routed && tid < kRec) s_rec[tid] = a.rec[(size_t)unit * kRec + tid];
+  // every candidate unit's record head (expert, first row, rows) in one round trip
+  if (tid < 3 * nmine) {
+    const int j = tid / 3, u = g + G * j;
+    if (u >= a.nsb) s_rec[j][tid % 3] = a.rec[(size_t)(u - a.nsb) * kRec + tid % 3];
+  }
   if (tid == 255) s_nact = a.n_active[0];
   if (!a.sep_combine) {
     for (int p = tid; p < n; p += 256) {
@@ -583,23 +606,44 @@ __global__ void __launch_bounds__(256) k_layer_down_combine(LayerArgs a) {
   }
   __syncthreads();
   const int n0 = slice * a.rd, n1 = min(H, n0 + a.rd);
-  if (routed) {
-    const int e = s_rec[0];
-    if (e < 0) return;
-    down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.down, e, s_rec[1], s_rec[1] + s_rec[2], n0, n1, a.h_routed,
-                                             a.o_routed, a.lpr_i, !a.sep_combine, smem);
-  } else {
-    const int r0 = unit * NT;
-    down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared,
-                                             a.lpr_is, !a.sep_combine, smem);
+  int done = 0;  // units of this slice this block projected
+  if constexpr (LOOP) {
+    for (int j = 0; j < nmine; ++j) {
+      // one projection site for both kinds of unit (the matrix and buffers picked per unit)
+      const int u = g + G * j;
+      const bool sh = u < a.nsb;
+      int e = 0, r0 = u * NT, r1 = min(T, r0 + NT);
+      if (!sh) {
+        e = s_rec[j][0];
+        if (e < 0) break;  // past the last touched expert (records are in unit order)
+        r0 = s_rec[j][1];
+        r1 = r0 + s_rec[j][2];
+      }
+      down_rows<FMT, NT, IP, down_lpr(NT, IP)>(sh ? a.sdown : a.down, e, r0, r1, n0, n1,
+                                               sh ? a.h_shared : a.h_routed, sh ? a.o_shared : a.o_routed,
+                                               sh ? a.lpr_is : a.lpr_i, !a.sep_combine, smem);
+      ++done;
+    }
+  } else if (nmine > 0) {
+    if (g >= a.nsb) {
+      const int e = s_rec[0][0];
+      if (e < 0) return;  // past the last touched expert
+      down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.down, e, s_rec[0][1], s_rec[0][1] + s_rec[0][2], n0, n1,
+                                               a.h_routed, a.o_routed, a.lpr_i, !a.sep_combine, smem);
+    } else {
+      const int r0 = g * NT;
+      down_rows<FMT, NT, IP, down_lpr(NT, IP)>(a.sdown, 0, r0, min(T, r0 + NT), n0, n1, a.h_shared, a.o_shared,
+                                               a.lpr_is, !a.sep_combine, smem);
+    }
+    done = 1;
   }
-  if (a.sep_combine) return;  // the combine launch reads the outputs after this launch
+  if (a.sep_combine || done == 0) return;  // a combine launch reads the outputs after this launch
   block_stores_done();
   const int units = s_nact + a.nsb;
   int* ctr = a.sync + kTicketSlice + 16 * slice;
-  if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) ticket = __hip_atomic_fetch_add(ctr, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (ticket != units - 1) return;
+  if (ticket + done != units) return;
   // last block of this slice: every unit's rows [n0, n1) are stored
   if (tid == 0) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -838,7 +882,12 @@ struct DecodeLds {
   size_t route, gateup, down;
 };
 
-static int router_tokens(int T) { return std::min(kRouteT, T); }
+// Tokens per router batch.  Up to kRouteOneT tokens each token is a batch of its own: the
+// batches' last blocks then rank their tokens in parallel, each with all four waves
+// (measured against batches of 4: 4 tokens 33.5 -> 32.6 us, the 8-token 47-layer chain
+// 2294 -> 2238 us; the router weights are read once per token batch, from the caches).
+constexpr int kRouteOneT = 8;
+static int router_tokens(int T) { return T <= kRouteOneT ? 1 : std::min(kRouteT, T); }
 
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
@@ -932,8 +981,8 @@ static hipError_t launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream
     MOE_LAUNCH((k_layer_down_t1<FMT, IP>), dim3((a.H + a.rows_t1 - 1) / a.rows_t1), dim3(kT1Threads), l1, s, a);
     return hipSuccess;
   }
-  MOE_LAUNCH((k_layer_down_combine<FMT, NT, GP, IP>), dim3((a.max_active + a.nsb) * a.slices_d), dim3(256),
-             lds.down, s, a);
+  const int groups = down_loops(FMT, NT, IP) ? a.down_groups : a.max_active + a.nsb;
+  MOE_LAUNCH((k_layer_down_combine<FMT, NT, GP, IP>), dim3(groups * a.slices_d), dim3(256), lds.down, s, a);
   if (!a.sep_combine) return hipSuccess;
   return launch_combine(a.o_routed, a.pair_pos, a.w, a.nsb > 0 ? a.o_shared : nullptr, a.residual, a.T, a.k, a.H,
                         a.y, nullptr, s);
@@ -1019,6 +1068,14 @@ hipError_t launch_layer_decode(const moe_layer_weights* L, const uint16_t* x, co
   // many tokens: the last down block of each slice would combine T x 64 outputs at the
   // launch's end (a serial tail); a combine launch of its own spreads that over the chip
   a.sep_combine = T > kSepCombineT;
+  {
+    // the looping down kernel: one unit per block while the units' slices fit kDownBlocks,
+    // above that each block takes several units of its slice (their record heads in one
+    // round trip, one slice ticket per block)
+    const int max_units = a.max_active + a.nsb;
+    const int fit = std::max(1, kDownBlocks / a.slices_d);
+    a.down_groups = std::min(max_units, std::max(fit, (max_units + kMaxDownUnits - 1) / kMaxDownUnits));
+  }
   // NVFP4, few tokens: the first launch's critical path is the router and its routing tail;
   // the shared expert's gate/up then runs beside the routed gate/up instead (measured, same
   // box: 1 token 19.7 -> 19.3 us, 4 tokens 33.4 -> 33.0 us, the 8-token chain -0.8%; at 16

@@ -461,6 +461,11 @@ LAYER_CASES = [
     ("flint_bf16_T16", 4, 2048, 768, 256, 6, 16, 31, True),
     ("tiny_bf16_T64", 4, 256, 128, 32, 6, 64, 32, False),
     ("ragged_bf16_H192_I320_T1", 4, 192, 320, 8, 6, 1, 33, True),
+    # 2 to 4 tokens: each gate/up block groups the pairs itself (one-token
+    # router batches), up to 1024 experts and k = 8
+    ("wide_E1024_k8_T4", 1, 256, 128, 1024, 8, 4, 34, True),
+    ("tiny_nvfp4_T3", 1, 256, 128, 32, 6, 3, 35, False),
+    ("ragged_int4_H192_I320_T2", 2, 192, 320, 8, 6, 2, 36, True),
 ]
 
 

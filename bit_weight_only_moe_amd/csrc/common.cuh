@@ -70,10 +70,21 @@ MOE_DEV moe_bf16x2 e2m1x2_to_bf16(uint32_t word) {
 // magic: 0x43004300 (the bf16 pair (128, 128)) held in a VGPR (int4_magic()):
 // with both constants literal the compiler emits an AND and an OR (CDNA's
 // three-operand encoding takes no literal), with the magic in a register a
-// single v_and_or_b32.
+// single v_and_or_b32 (the mask goes in a scalar register).  Written as an
+// asm statement (no side effects, so still scheduled freely): in plain C the
+// compiler unpacks every resident piece as soon as its codes arrive, which
+// held the multi-token gate/up kernels compiled for the Flint shape at 128
+// registers with 73 spilled and the down kernel at 180; as asm they take 106
+// and 108 and spill nothing.
 template <int S>
 MOE_DEV moe_bf16x2 int4x2_to_bf16_off128(uint32_t word, uint32_t magic) {
-  uint32_t v = ((word >> (4 * S)) & 0x000F000Fu) | magic;
+  uint32_t v;
+  if constexpr (S == 0)
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(v) : "v"(word), "s"(0x000F000Fu), "v"(magic));
+  else
+    asm("v_lshrrev_b32 %0, %4, %1\n\tv_and_or_b32 %0, %0, %2, %3"
+        : "=&v"(v)
+        : "v"(word), "s"(0x000F000Fu), "v"(magic), "i"(4 * S));
   return __builtin_bit_cast(moe_bf16x2, v);
 }
 

@@ -11,21 +11,25 @@
 // the final ticket continues with a device-scope acquire.
 //
 //   launch 1  router blocks: logits of 4 experts (one per wave) for a batch
-//             of up to 4 tokens.  The last router block of a batch does the
-//             batch's top-k + softmax (one token per wave); the last batch to
-//             finish groups every (token, choice) pair by expert and writes
-//             one record per touched expert.  Shared-expert blocks (same
+//             of tokens (one token up to 8 tokens, else up to 4).  The last
+//             router block of a batch does the batch's top-k + softmax (a lone
+//             token with all four waves, else one token per wave); the last
+//             batch to finish groups every (token, choice) pair by expert and
+//             writes one record per touched expert (from 2 to 4 tokens the
+//             gate/up blocks group instead).  Shared-expert blocks (same
 //             grid): gate/up + SwiGLU, which needs no routing, so its weights
 //             stream while the router runs.
 //   launch 2  routed gate/up + SwiGLU: one (record, row slice of I) per
 //             block; each touched expert's weights are read once for all the
 //             tokens that chose it.
 //   launch 3  down projection: one (unit = record or shared-expert token
-//             batch, row slice of H) per block, fp32 outputs to the
-//             workspace; the last block of each slice combines
-//             y = residual + sum_j w_j o_j + o_shared in that fixed order and
-//             rounds to bf16.  A lone token instead: each block takes a few
-//             output rows of every unit and combines them in LDS itself.
+//             batch, row slice of H) per block (NVFP4 at 2 to 16 tokens:
+//             about 1024 blocks, each taking several units of its slice),
+//             fp32 outputs to the workspace; the last block of each slice
+//             combines y = residual + sum_j w_j o_j + o_shared in that fixed
+//             order and rounds to bf16.  A lone token instead: each block
+//             takes a few output rows of every unit and combines them in LDS
+//             itself.
 //
 // Every block loads all of its weight pieces before it uses any, so one
 // memory round trip covers a block's whole share of the expert bytes.
@@ -1089,13 +1093,12 @@ static hipError_t launch_all(const LayerArgs& a, const DecodeLds& lds, hipStream
 // The Flint shape (hidden 2048, inter 768, the shared expert as wide as the
 // routed ones) runs kernels compiled for it; every other shape the same
 // kernels with its runtime shape.  Measured (NVFP4, 1/4/16/64 tokens):
-// 21.9/38.8/78.3/190 -> 20.4/34.6/68.1/148 us.  INT4 with several tokens
-// keeps the runtime shape: compiled for the Flint shape its gate/up spills
-// (78 registers at its 128-register bound) and its down needs 180
-// registers, 2.6x slower; one INT4 token gains (24.3 -> 21.4 us).
+// 21.9/38.8/78.3/190 -> 20.4/34.6/68.1/148 us.  The INT4 forms fit their
+// register bounds compiled for the Flint shape since their nibble unpack is
+// an asm statement (int4x2_to_bf16_off128).
 template <int FMT, int NT>
 static hipError_t launch_shape(const LayerArgs& a, const DecodeLds& lds, hipStream_t s) {
-  if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && FMT != kFmtBf16 && (FMT == kFmtNvfp4 || NT == 1))
+  if (a.H == 2048 && a.I == 768 && (a.Is == 0 || a.Is == 768) && FMT != kFmtBf16)
     return launch_all<FMT, NT, 64, 24>(a, lds, s);
   return launch_all<FMT, NT, 0, 0>(a, lds, s);
 }

@@ -61,9 +61,9 @@ WARM_MS = 50.0            # untimed graph replays queued right before the timed 
 # Workloads not listed report null.
 TRAFFIC_BYTES = {
     ("decode_b1", "nvfp4"): 21.53e6,
-    ("decode_T16", "nvfp4"): 221.8e6,
+    ("decode_T16", "nvfp4"): 221.5e6,
     ("decode_T64", "nvfp4"): 560.2e6,
-    ("chain_b8", "nvfp4"): 5.90e9,
+    ("chain_b8", "nvfp4"): 5.89e9,
     ("dense_head_T1", "nvfp4"): 173.7e6,
     ("dense_head_T8", "nvfp4"): 214.6e6,
     ("prefill", "nvfp4"): 1236.6e6,

@@ -15,7 +15,7 @@
 //             router block of a batch does the batch's top-k + softmax (a lone
 //             token with all four waves, else one token per wave); the last
 //             batch to finish groups every (token, choice) pair by expert and
-//             writes one record per touched expert (from 2 to 4 tokens the
+//             writes one record per touched expert (from 2 to 8 tokens the
 //             gate/up blocks group instead).  Shared-expert blocks (same
 //             grid): gate/up + SwiGLU, which needs no routing, so its weights
 //             stream while the router runs.
@@ -59,11 +59,12 @@ constexpr bool fmt_shared_early(int fmt) { return fmt == kFmtNvfp4; }
 constexpr int kRouteT = 4;   // tokens per router block (a batch; its last block routes them, one per wave)
 constexpr int kMaxBatches = 16;  // 64 tokens / kRouteT
 constexpr int kRec = 4 + 64; // ints per routed-unit record: expert, first row, rows, 0, token[rows]
-// From 2 to kGroupInGateupT tokens each gate/up block groups the pairs it needs
-// itself instead of one block at the end of launch 1 (measured: 4 tokens 32.8 ->
-// 31.3 us; at 8 and 16 tokens, with two to four rounds of gate/up blocks, the
-// per-block grouping costs more than the first launch saves: +0.5% and +2.5%).
-constexpr int kGroupInGateupT = 4;
+// From 2 to kGroupInGateupT tokens one wave of each gate/up block groups the
+// pairs it needs itself instead of one block at the end of launch 1 (measured:
+// 4 tokens 32.8 -> 31.3 us; the 8-token chain 2147 -> 2113 us once the grouping
+// took one wave and no block barriers; with the four-wave grouping 8 and 16
+// tokens lost 0.5% and 2.5%).  At most 8 tokens: the T*k <= 64 pairs fit one wave.
+constexpr int kGroupInGateupT = 8;
 // Down blocks of the looping down kernel: about four blocks per CU, each taking
 // several units of its slice (measured against one unit per block, the 8-token
 // 47-layer chain 2238 -> 2148 us, 16 tokens 66.4 -> 63.9 us; at 64 tokens and in
@@ -434,7 +435,7 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
   __syncthreads();
   const int p0 = t0 * k, p1 = (t0 + nt) * k;  // this batch's pairs
   if (NT == 2 && T <= kGroupInGateupT) {
-    // each gate/up block groups the pairs it needs itself (group_unit), so this
+    // each gate/up block groups the pairs it needs itself (group_unit_wave), so this
     // batch only publishes its choices for the next launch
     for (int p = p0 + tid; p < p1; p += 256) {
       a.ids[p] = s_ids[p];
@@ -560,69 +561,56 @@ __global__ void __launch_bounds__(256) k_layer_route_shared(LayerArgs a) {
 }
 
 // ------------------------------------------------------------------ grouping in launch 2
-// Record of unit u (the u-th smallest touched expert) built by one gate/up
-// block from the T*k <= 128 chosen ids of every token: the same expert, first
-// grouped row, row count and token list (ascending tokens) that a single
-// grouping block would write, so the grouped order is unchanged.  The block of
-// each unit's first slice (`publish`) also stores the record and its pairs'
-// grouped rows for the down launch, and unit 0's block the number of touched
-// experts.  Units past the last touched expert get expert -1.  All threads
-// call; s_rec is this block's LDS copy (valid after the caller's barrier).
-MOE_DEV void group_unit(const LayerArgs& a, int u, bool publish, int* s_rec) {
-  __shared__ uint32_t s_mask[32];  // touched experts, E <= 1024
-  __shared__ int s_lt[4], s_eq[4], s_e;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Record of unit u (the u-th smallest touched expert) built by one wave of a
+// gate/up block from the T*k <= 64 chosen ids of every token (one pair per
+// lane): the same expert, first grouped row, row count and token list
+// (ascending tokens) that a single grouping block would write, so the grouped
+// order is unchanged.  The block of each unit's first slice (`publish`) also
+// stores the record and its pairs' grouped rows for the down launch, and unit
+// 0's block the number of touched experts.  Units past the last touched
+// expert get expert -1.  Called by wave 0 only (the wave's LDS traffic is in
+// order, so no block barrier); s_rec is the block's LDS copy, valid after the
+// caller's barrier.
+MOE_DEV void group_unit_wave(const LayerArgs& a, int u, bool publish, int* s_rec, uint32_t* s_mask) {
+  const int lane = threadIdx.x & 63;
   const int k = a.k, n = a.T * k;
-  const int id = tid < n ? a.ids[tid] : -1;
-  if (tid < 32) s_mask[tid] = 0u;
-  __syncthreads();
+  const int id = lane < n ? a.ids[lane] : -1;
+  if (lane < 32) s_mask[lane] = 0u;  // touched experts, E <= 1024
+  wave_lds_sync();
   if (id >= 0) atomicOr(&s_mask[id >> 5], 1u << (id & 31));
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t m = lane < 32 ? s_mask[lane] : 0u;
-    const int c = __popc(m);
-    const int inc = wave_inclusive_scan(c);
-    const int total = __shfl(inc, 63, 64);
-    if (inc - c <= u && u < inc) {
-      uint32_t mm = m;  // drop the set bits below the wanted one
-      for (int q = u - (inc - c); q > 0; --q) mm &= mm - 1u;
-      s_e = lane * 32 + __ffs(mm) - 1;
-    }
-    if (lane == 0) {
-      if (u >= total) s_e = -1;
-      if (publish && u == 0) a.n_active[0] = total;
-    }
+  wave_lds_sync();
+  const uint32_t m = lane < 32 ? s_mask[lane] : 0u;
+  const int c = __popc(m);
+  const int inc = wave_inclusive_scan(c);
+  const int total = __shfl(inc, 63, 64);
+  int mine = -1;
+  if (inc - c <= u && u < inc) {
+    uint32_t mm = m;  // drop the set bits below the wanted one
+    for (int q = u - (inc - c); q > 0; --q) mm &= mm - 1u;
+    mine = lane * 32 + __ffs(mm) - 1;
   }
-  __syncthreads();
-  const int e = s_e;
+  const uint64_t who = __ballot(mine >= 0);
+  const int e = who ? __shfl(mine, __ffsll((long long)who) - 1, 64) : -1;
+  if (publish && u == 0 && lane == 0) a.n_active[0] = total;
+  int32_t* rec = a.rec + (size_t)u * kRec;
   if (e < 0) {
-    if (publish && tid == 0) a.rec[(size_t)u * kRec] = -1;
-    if (tid == 0) s_rec[0] = -1;
+    if (lane == 0) {
+      s_rec[0] = -1;
+      if (publish) rec[0] = -1;
+    }
     return;
   }
-  const uint64_t blt = __ballot(id >= 0 && id < e), beq = __ballot(id == e);
-  if (lane == 0) {
-    s_lt[wave] = __popcll(blt);
-    s_eq[wave] = __popcll(beq);
-  }
-  __syncthreads();
-  int r0 = 0, cnt = 0, before = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    r0 += s_lt[w];
-    cnt += s_eq[w];
-    before += w < wave ? s_eq[w] : 0;
-  }
-  int32_t* rec = a.rec + (size_t)u * kRec;
+  const uint64_t beq = __ballot(id == e);
+  const int r0 = __popcll(__ballot(id >= 0 && id < e)), cnt = __popcll(beq);
   if (id == e) {
-    const int rank = before + __popcll(beq & ((1ull << lane) - 1ull));
-    s_rec[4 + rank] = tid / k;
+    const int rank = __popcll(beq & ((1ull << lane) - 1ull));
+    s_rec[4 + rank] = lane / k;
     if (publish) {
-      rec[4 + rank] = tid / k;
-      a.pair_pos[tid] = r0 + rank;
+      rec[4 + rank] = lane / k;
+      a.pair_pos[lane] = r0 + rank;
     }
   }
-  if (tid == 0) {
+  if (lane == 0) {
     s_rec[0] = e;
     s_rec[1] = r0;
     s_rec[2] = cnt;
@@ -656,9 +644,10 @@ __global__ void __launch_bounds__(256, FMT != kFmtNvfp4 && NT > 1 ? 4 : 1) k_lay
     return;
   }
   const int unit = (blockIdx.x - nsh) / a.slices_r;
-  if (NT == 2 && a.T <= kGroupInGateupT)
-    group_unit(a, unit, (blockIdx.x - nsh) % a.slices_r == 0, s_rec);
-  else if (threadIdx.x < kRec)
+  if (NT == 2 && a.T <= kGroupInGateupT) {
+    __shared__ uint32_t s_mask[32];
+    if (threadIdx.x < 64) group_unit_wave(a, unit, (blockIdx.x - nsh) % a.slices_r == 0, s_rec, s_mask);
+  } else if (threadIdx.x < kRec)
     s_rec[threadIdx.x] = a.rec[(size_t)unit * kRec + threadIdx.x];
   __syncthreads();
   const int e = s_rec[0];

@@ -466,6 +466,10 @@ LAYER_CASES = [
     ("wide_E1024_k8_T4", 1, 256, 128, 1024, 8, 4, 34, True),
     ("tiny_nvfp4_T3", 1, 256, 128, 32, 6, 3, 35, False),
     ("ragged_int4_H192_I320_T2", 2, 192, 320, 8, 6, 2, 36, True),
+    # 2 to 4 tokens at the Flint shape: the down launch that combines in LDS
+    ("flint_nvfp4_T2", 1, 2048, 768, 256, 6, 2, 37, True),
+    ("flint_int4_T3", 2, 2048, 768, 256, 6, 3, 38, False),
+    ("flint_int4sb_T2_k8", 3, 2048, 768, 256, 8, 2, 39, True),
 ]
 
 

@@ -22,7 +22,8 @@ the flush and the timed replay (between HIP events on the launch stream)
 are queued back to back, so the timed steps start on a busy chip.
 
 The sweep also carries the dense 4-bit output-head GEMV (150,144 x 2048,
-1 and 8 tokens).
+1 and 8 tokens).  ``process_spread`` times the headline workload again in
+fresh processes (``--spread-processes``, default 2).
 
 Single workloads (``--workload``): decode_b1, decode_T4, decode_T16,
 decode_T64 (with ``--fmt int4`` or ``--fmt int4sb`` for the other formats), chain_b8, prefill,
@@ -80,6 +81,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the headline's CPU oracle leg")
     p.add_argument("--sweep-cpu-seconds", type=float, default=3.0, help="time budget of each sweep entry's oracle leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--spread-processes", type=int, default=2,
+                   help="fresh processes that time the headline workload again (0: none)")
     p.add_argument("--tokens", type=int, default=1, help="tokens of the dense_head workload")
     p.add_argument("--eager", action="store_true",
                    help="launch the K timed steps directly instead of replaying a captured graph (profiler runs)")
@@ -500,6 +503,25 @@ def line_from(entry, fmt_name, value_key, unit, K, W):
             "roofline": entry["roofline"], "cpu_baseline": entry["cpu_baseline"]}
 
 
+def process_spread(args, head_ms, K, W):
+    """The headline workload timed again in fresh processes, each with its own
+    weight copies and tokens: the spread between processes, next to the one in
+    this process."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "decode_b1", "--fmt", "nvfp4",
+           "--steps", str(K), "--warmup", str(W), "--no-cpu-baseline"]
+    vals = [head_ms]
+    for _ in range(args.spread_processes):
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            return {"error": "a spread process failed (exit %d)" % r.returncode, "ms_per_step": vals}
+        vals.append(json.loads(lines[-1])["ms_per_step"])
+    med = float(np.median(vals))
+    return {"processes": len(vals), "ms_per_step": vals, "median_ms": med,
+            "spread": (max(vals) - min(vals)) / med}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -562,6 +584,9 @@ def main():
         print("[bench] dense head T=%d done (%.0f s)" % (T, time.perf_counter() - t_start), file=sys.stderr,
               flush=True)
     out = line_from(head, "nvfp4", "tokens_per_s", "tokens/s", K, W)
+    if args.spread_processes > 0:
+        out["process_spread"] = process_spread(args, out["ms_per_step"], K, W)
+        print("[bench] process spread done (%.0f s)" % (time.perf_counter() - t_start), file=sys.stderr, flush=True)
     out["sweep"] = sweep
     print(json.dumps(out))
 

@@ -470,6 +470,9 @@ LAYER_CASES = [
     ("flint_nvfp4_T2", 1, 2048, 768, 256, 6, 2, 37, True),
     ("flint_int4_T3", 2, 2048, 768, 256, 6, 3, 38, False),
     ("flint_int4sb_T2_k8", 3, 2048, 768, 256, 8, 2, 39, True),
+    # 8 tokens with k = 8: 64 pairs, one per lane of the grouping wave
+    ("wide_E1024_k8_T8", 1, 256, 128, 1024, 8, 8, 40, True),
+    ("flint_int4sb_T8_k8", 3, 2048, 768, 256, 8, 8, 41, False),
 ]
 
 

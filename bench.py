@@ -61,8 +61,8 @@ WARM_MS = 50.0            # untimed graph replays queued right before the timed 
 # counters read 1 GiB each for a plain 1 GiB device copy (profiles/hbm_traffic_counters.md).
 # Workloads not listed report null.
 TRAFFIC_BYTES = {
-    ("decode_b1", "nvfp4"): 21.51e6,
-    ("decode_T16", "nvfp4"): 221.6e6,
+    ("decode_b1", "nvfp4"): 21.52e6,
+    ("decode_T16", "nvfp4"): 221.5e6,
     ("decode_T64", "nvfp4"): 560.2e6,
     ("chain_b8", "nvfp4"): 5.89e9,
     ("dense_head_T1", "nvfp4"): 173.7e6,

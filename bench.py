@@ -62,8 +62,10 @@ WARM_MS = 50.0            # untimed graph replays queued right before the timed 
 # Workloads not listed report null.
 TRAFFIC_BYTES = {
     ("decode_b1", "nvfp4"): 21.52e6,
+    ("decode_T4", "nvfp4"): 68.6e6,
     ("decode_T16", "nvfp4"): 221.5e6,
-    ("decode_T64", "nvfp4"): 560.2e6,
+    ("decode_T16", "int4"): 215.8e6,
+    ("decode_T64", "nvfp4"): 559.8e6,
     ("chain_b8", "nvfp4"): 5.89e9,
     ("dense_head_T1", "nvfp4"): 173.7e6,
     ("dense_head_T8", "nvfp4"): 214.6e6,
